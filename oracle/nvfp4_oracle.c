@@ -1,0 +1,503 @@
+/*
+ * nvfp4_oracle.c -- plain CPU reference for NVFP4 block quantization.
+ * TEST INFRASTRUCTURE ONLY (see nvfp4_oracle.h): never called by the product path.
+ *
+ * Build: gcc -std=c11 -O2 -ffp-contract=off -fno-fast-math -fPIC -shared -pthread
+ *
+ * Every floating-point step below is written as one binary32 operation in the
+ * order stated; fl(.) in the comments means "rounded to binary32, to nearest
+ * even".  Steps with a plain mathematical definition (nearest point of a finite
+ * grid) are evaluated exactly in binary64.
+ */
+#include "nvfp4_oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Number formats                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* bf16 is the upper half of a binary32 pattern: widening is exact. */
+float orc_bf16_to_f32(uint16_t h) {
+  uint32_t b = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &b, 4);
+  return f;
+}
+
+/* The E2M1 magnitudes.  [P2] "Problem statement": steps of 0.5 on [0,2],
+ * 1 on [2,4] and 2 on [4,6]; the largest value is 6. */
+static const double kE2M1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+static int sign_bit(float z) {
+  uint32_t b;
+  memcpy(&b, &z, 4);
+  return (int)(b >> 31);
+}
+
+/* Round to nearest E2M1 magnitude; on an exact tie take the even grid index.
+ * Anything at or beyond 6 is nearest to 6 (taken directly: for huge |z| the
+ * binary64 differences below would no longer be exact).
+ * The sign bit of z is kept, so -0 and small negatives give code 0x8. */
+uint8_t orc_e2m1_rne(float z) {
+  double a = fabs((double)z);
+  if (a >= 6.0) return (uint8_t)((sign_bit(z) << 3) | 7);
+  int best = 0;
+  double bestd = fabs(a - kE2M1[0]);
+  for (int k = 1; k < 8; ++k) {
+    double d = fabs(a - kE2M1[k]); /* exact: a < 6 is binary32, grid points are dyadic */
+    if (d < bestd || (d == bestd && (k % 2) == 0)) {
+      best = k;
+      bestd = d;
+    }
+  }
+  return (uint8_t)((sign_bit(z) << 3) | best);
+}
+
+/* Stochastic rounding ([P1] section 2d): between the two neighbouring grid
+ * points lo <= |z| < hi, round up with probability equal to the fractional
+ * distance f = (|z| - lo) / (hi - lo).  Reading used here: the decision takes
+ * the top 22 bits u of the random word and the fraction truncated to 22 bits,
+ * F = floor(f * 2^22), and rounds up iff u + F >= 2^22; so P(up) = F / 2^22,
+ * which is f to within 2^-22.  |z| >= 6 gives 6; grid points are never moved. */
+uint8_t orc_e2m1_sr(float z, uint32_t rword) {
+  double a = fabs((double)z);
+  int s = sign_bit(z);
+  if (a >= 6.0) return (uint8_t)((s << 3) | 7);
+  int k = 0;
+  for (int i = 0; i < 8; ++i)
+    if (kE2M1[i] <= a) k = i;
+  double f = (a - kE2M1[k]) / (kE2M1[k + 1] - kE2M1[k]); /* exact: dyadic operands, power-of-two divisor */
+  uint32_t F = (uint32_t)floor(f * 4194304.0);
+  uint32_t u = rword >> 10;
+  int up = (u + F) >= 4194304u;
+  return (uint8_t)((s << 3) | (k + up));
+}
+
+float orc_e2m1_value(uint8_t code) {
+  double v = kE2M1[code & 7];
+  return (float)((code & 8) ? -v : v);
+}
+
+/* E4M3 (OCP "E4M3FN"): 1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ * subnormals m * 2^-9; largest finite value 448 = 0x7E; 0x7F is NaN. */
+float orc_e4m3_value(uint8_t code) {
+  int e = (code >> 3) & 15, m = code & 7;
+  double v = (e == 0) ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+  return (float)((code & 0x80) ? -v : v);
+}
+
+/* Round half to even to an integer, exactly (q is exact in binary64). */
+static double rne_int(double q) {
+  double fl = floor(q);
+  double d = q - fl;
+  if (d > 0.5) return fl + 1.0;
+  if (d < 0.5) return fl;
+  return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;
+}
+
+/* Encode r >= 0 as the nearest E4M3 value (ties to even mantissa), saturating
+ * at 448: everything at or above 448, including +inf, gives 0x7E. */
+uint8_t orc_e4m3_rne_sat(float r) {
+  double x = (double)r;
+  if (!(x < 448.0)) return 0x7E;
+  if (x < ldexp(1.0, -6)) {
+    /* subnormal binade: quantum 2^-9; n = 8 lands on 2^-6 = code 0x08 */
+    double n = rne_int(x * 512.0);
+    return (uint8_t)n;
+  }
+  int e2;
+  frexp(x, &e2);
+  int E = e2 - 1; /* x in [2^E, 2^(E+1)), E in [-6, 8] */
+  double q = ldexp(x, 3 - E); /* in [8, 16) */
+  double n = rne_int(q);
+  if (n == 16.0) {
+    n = 8.0;
+    E += 1;
+  }
+  if (E > 8 || (E == 8 && n > 14.0)) return 0x7E;
+  return (uint8_t)(((E + 7) << 3) | ((int)n - 8));
+}
+
+/* ------------------------------------------------------------------------ */
+/* Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as   */
+/* easy as 1, 2, 3", SC'11): ten rounds of two 32x32->64 multiplications with */
+/* the published multipliers, the key bumped by the published Weyl constants  */
+/* between rounds.                                                            */
+/* ------------------------------------------------------------------------ */
+void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+  const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+  uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+  uint32_t k0 = key[0], k1 = key[1];
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += W0;
+      k1 += W1;
+    }
+    uint64_t p0 = (uint64_t)M0 * c0;
+    uint64_t p1 = (uint64_t)M1 * c2;
+    uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    uint32_t n1 = (uint32_t)p1;
+    uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    uint32_t n3 = (uint32_t)p0;
+    c0 = n0;
+    c1 = n1;
+    c2 = n2;
+    c3 = n3;
+  }
+  out[0] = c0;
+  out[1] = c1;
+  out[2] = c2;
+  out[3] = c3;
+}
+
+/* One 32-bit word per element: key = (seed low, seed high); counter =
+ * (q low, q high, 0, 0) with q = idx / 4; the word is output (idx mod 4). */
+uint32_t orc_sr_word(uint64_t seed, uint64_t idx) {
+  uint64_t q = idx >> 2;
+  uint32_t ctr[4] = {(uint32_t)q, (uint32_t)(q >> 32), 0u, 0u};
+  uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t out[4];
+  orc_philox4x32_10(ctr, key, out);
+  return out[idx & 3];
+}
+
+/* Sign mask for the Hadamard transform: low 16 bits of word 0 at counter
+ * (0, 0, 0, 1).  The stochastic-rounding stream always has counter word 3 = 0,
+ * so the two streams never share a counter. */
+uint32_t orc_rht_mask_from_seed(uint64_t seed) {
+  uint32_t ctr[4] = {0u, 0u, 0u, 1u};
+  uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t out[4];
+  orc_philox4x32_10(ctr, key, out);
+  return out[0] & 0xFFFFu;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 16-point random Hadamard transform ([P1] section 2b): y = H16 * D * x / 4  */
+/* with H16 the Sylvester Hadamard matrix in natural order and D = diag(+-1). */
+/* Stages h = 1, 2, 4, 8; in each, pairs (i, i+h) with (i & h) == 0 become    */
+/* (fl(a+b), fl(a-b)); then every value is multiplied by 0.25 (exact).        */
+/* ------------------------------------------------------------------------ */
+void orc_rht16(const float* x, uint32_t mask, float* y) {
+  float v[16];
+  for (int i = 0; i < 16; ++i) v[i] = ((mask >> i) & 1u) ? -x[i] : x[i];
+  for (int h = 1; h < 16; h <<= 1) {
+    for (int i = 0; i < 16; ++i) {
+      if (i & h) continue;
+      float a = v[i], b = v[i + h];
+      v[i] = a + b;
+      v[i + h] = a - b;
+    }
+  }
+  for (int i = 0; i < 16; ++i) y[i] = 0.25f * v[i];
+}
+
+/* ------------------------------------------------------------------------ */
+/* Block quantization ([P2] "Core mechanism", "Adaptive block scaling")      */
+/* ------------------------------------------------------------------------ */
+
+/* Pairwise sum in index order: (t0+t1), (t2+t3), ..., then pairs of those. */
+static float pairwise_sum(const float* t, int n) {
+  if (n == 1) return t[0];
+  int h = n / 2;
+  float a = pairwise_sum(t, h);
+  float b = pairwise_sum(t + h, h);
+  return a + b;
+}
+
+/* One candidate: scale the block's max to T (6, or 4 for the 4/6 alternative).
+ *   den = fl(T * s_t); r = fl(m_b / den) (0 if m_b or den is 0)
+ *   sb  = E4M3(r);     d = fl(dec(sb) * s_t); e = fl(1 / d) (0 if d is 0 or 1/d overflows)
+ *   z_i = fl(y_i * e); code_i = round(z_i)
+ * With rule != NONE, the error against the values being quantized
+ * ([P2] "Adaptive block scaling", step 2) is
+ *   xh_i = fl(value(code_i) * d); eps_i = fl(y_i - xh_i)
+ *   MSE: pairwise sum of fl(eps_i * eps_i); MAE: pairwise sum of |eps_i|; MAXERR: max |eps_i|. */
+static void candidate(const float* y, int n, float m_b, float T, float s_t, int rule, int sr,
+                      const uint32_t* rwords, uint8_t* codes, uint8_t* sb_out, float* err) {
+  float den = T * s_t;
+  float r = (m_b == 0.0f || den == 0.0f) ? 0.0f : m_b / den;
+  uint8_t sb = orc_e4m3_rne_sat(r);
+  float d = orc_e4m3_value(sb) * s_t;
+  float e = 0.0f;
+  if (d != 0.0f) {
+    e = 1.0f / d;
+    if (isinf(e)) e = 0.0f;
+  }
+  for (int i = 0; i < n; ++i) {
+    float z = y[i] * e;
+    codes[i] = sr ? orc_e2m1_sr(z, rwords[i]) : orc_e2m1_rne(z);
+  }
+  *sb_out = sb;
+  *err = 0.0f;
+  if (rule == ORC_RULE_NONE) return;
+  float t[256];
+  float mx = 0.0f;
+  for (int i = 0; i < n; ++i) {
+    float xh = orc_e2m1_value(codes[i]) * d;
+    float eps = y[i] - xh;
+    float ae = fabsf(eps);
+    if (rule == ORC_RULE_MSE) t[i] = eps * eps;
+    else t[i] = ae;
+    if (ae > mx) mx = ae;
+  }
+  *err = (rule == ORC_RULE_MAXERR) ? mx : pairwise_sum(t, n);
+}
+
+void orc_quantize_block(const float* y, int n, float s_t, int rule, int sr, const uint32_t* rwords,
+                        uint8_t* codes, uint8_t* scale, uint8_t* chose4, float* err) {
+  float m_b = 0.0f;
+  for (int i = 0; i < n; ++i) {
+    float a = fabsf(y[i]);
+    if (a > m_b) m_b = a;
+  }
+  uint8_t c6[256], sb6;
+  float e6;
+  candidate(y, n, m_b, 6.0f, s_t, rule, sr, rwords, c6, &sb6, &e6);
+  err[0] = e6;
+  err[1] = 0.0f;
+  *chose4 = 0;
+  if (rule != ORC_RULE_NONE) {
+    uint8_t c4[256], sb4;
+    float e4;
+    candidate(y, n, m_b, 4.0f, s_t, rule, sr, rwords, c4, &sb4, &e4);
+    err[1] = e4;
+    if (e4 < e6) { /* strict: a tie keeps the standard scale-to-6 block */
+      memcpy(codes, c4, (size_t)n);
+      *scale = sb4;
+      *chose4 = 1;
+      return;
+    }
+  }
+  memcpy(codes, c6, (size_t)n);
+  *scale = sb6;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Tensor level                                                               */
+/* ------------------------------------------------------------------------ */
+
+static float load_elem(const void* x, int dtype, int64_t i) {
+  if (dtype == ORC_IN_F32) return ((const float*)x)[i];
+  return orc_bf16_to_f32(((const uint16_t*)x)[i]);
+}
+
+/* The per-tensor amax behind the FP32 tensor scale ([P2] "Implementation
+ * details").  With the transform on, it is the amax of the transformed tensor. */
+float orc_amax(const void* x, int dtype, int64_t rows, int64_t cols, int rht, uint32_t mask) {
+  float A = 0.0f;
+  if (!rht) {
+    for (int64_t i = 0; i < rows * cols; ++i) {
+      float a = fabsf(load_elem(x, dtype, i));
+      if (a > A) A = a;
+    }
+    return A;
+  }
+  float in[16], out[16];
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t j = 0; j < cols / 16; ++j) {
+      for (int k = 0; k < 16; ++k) in[k] = load_elem(x, dtype, r * cols + j * 16 + k);
+      orc_rht16(in, mask, out);
+      for (int k = 0; k < 16; ++k) {
+        float a = fabsf(out[k]);
+        if (a > A) A = a;
+      }
+    }
+  }
+  return A;
+}
+
+/* S_t = fl(A / fl(6 * cap)); the block scale maps a block's max to
+ * 6 * dec(sb) * S_t, so the largest block lands on the E4M3 value `cap`. */
+float orc_tensor_scale(float amax, float cap) {
+  float c6 = 6.0f * cap;
+  return amax / c6;
+}
+
+typedef struct {
+  const void* x;
+  int dtype;
+  int64_t rows, cols, r0, r1;
+  const orc_config* cfg;
+  float s_t;
+  uint8_t *codes_row, *scales_row, *codes_col, *scales_col, *pick_row, *pick_col;
+} band_job;
+
+static void put_nibble(uint8_t* base, int64_t byte, int hi, uint8_t code) {
+  if (hi) base[byte] = (uint8_t)((base[byte] & 0x0F) | (code << 4));
+  else base[byte] = (uint8_t)((base[byte] & 0xF0) | (code & 0x0F));
+}
+
+static void fill_words(const orc_config* cfg, const int64_t* idx, int n, uint32_t* w) {
+  for (int i = 0; i < n; ++i) w[i] = cfg->sr ? orc_sr_word(cfg->sr_seed, (uint64_t)idx[i]) : 0u;
+}
+
+/* Rows [r0, r1) of the tensor; r0 and r1 are multiples of 16 whenever a
+ * column copy or 2D tiles are requested. */
+static void quantize_band(const band_job* J) {
+  const orc_config* cfg = J->cfg;
+  const int64_t M = J->rows, N = J->cols;
+  float y[256];
+  int64_t idx[256];
+  uint32_t w[256];
+  uint8_t codes[256], sb, ch;
+  float err[2];
+
+  if (cfg->block_2d) {
+    /* [P1] section 2c: one scale per 16x16 tile, shared by both orientations. */
+    for (int64_t ti = J->r0 / 16; ti < J->r1 / 16; ++ti) {
+      for (int64_t tj = 0; tj < N / 16; ++tj) {
+        for (int i = 0; i < 16; ++i)
+          for (int j = 0; j < 16; ++j) {
+            int64_t r = ti * 16 + i, c = tj * 16 + j;
+            y[i * 16 + j] = load_elem(J->x, J->dtype, r * N + c);
+            idx[i * 16 + j] = (cfg->row_offset + r) * N + c;
+          }
+        fill_words(cfg, idx, 256, w);
+        orc_quantize_block(y, 256, J->s_t, cfg->rule, cfg->sr, w, codes, &sb, &ch, err);
+        if (cfg->emit_row) {
+          J->scales_row[ti * (N / 16) + tj] = sb;
+          if (J->pick_row) J->pick_row[ti * (N / 16) + tj] = ch;
+          for (int i = 0; i < 16; ++i)
+            for (int j = 0; j < 16; ++j) {
+              int64_t r = ti * 16 + i, c = tj * 16 + j;
+              put_nibble(J->codes_row, r * (N / 2) + c / 2, (int)(c & 1), codes[i * 16 + j]);
+            }
+        }
+        if (cfg->emit_col) {
+          J->scales_col[tj * (M / 16) + ti] = sb;
+          if (J->pick_col) J->pick_col[tj * (M / 16) + ti] = ch;
+          for (int i = 0; i < 16; ++i)
+            for (int j = 0; j < 16; ++j) {
+              int64_t r = ti * 16 + i, c = tj * 16 + j;
+              put_nibble(J->codes_col, c * (M / 2) + r / 2, (int)(r & 1), codes[i * 16 + j]);
+            }
+        }
+      }
+    }
+    return;
+  }
+
+  if (cfg->emit_row) {
+    float in[16];
+    for (int64_t r = J->r0; r < J->r1; ++r) {
+      for (int64_t j = 0; j < N / 16; ++j) {
+        for (int k = 0; k < 16; ++k) {
+          in[k] = load_elem(J->x, J->dtype, r * N + j * 16 + k);
+          idx[k] = (cfg->row_offset + r) * N + j * 16 + k;
+        }
+        if (cfg->rht) orc_rht16(in, cfg->rht_mask, y);
+        else memcpy(y, in, sizeof(in));
+        fill_words(cfg, idx, 16, w);
+        orc_quantize_block(y, 16, J->s_t, cfg->rule, cfg->sr, w, codes, &sb, &ch, err);
+        J->scales_row[r * (N / 16) + j] = sb;
+        if (J->pick_row) J->pick_row[r * (N / 16) + j] = ch;
+        for (int k = 0; k < 16; ++k) put_nibble(J->codes_row, r * (N / 2) + (j * 16 + k) / 2, k & 1, codes[k]);
+      }
+    }
+  }
+  if (cfg->emit_col) {
+    /* [P1] section 2c: the backward pass needs the column orientation; here
+     * each column is cut into 16x1 blocks of the same values (same S_t). */
+    for (int64_t c = 0; c < N; ++c) {
+      for (int64_t i = J->r0 / 16; i < J->r1 / 16; ++i) {
+        for (int k = 0; k < 16; ++k) {
+          int64_t r = i * 16 + k;
+          y[k] = load_elem(J->x, J->dtype, r * N + c);
+          idx[k] = (cfg->row_offset + r) * N + c;
+        }
+        fill_words(cfg, idx, 16, w);
+        orc_quantize_block(y, 16, J->s_t, cfg->rule, cfg->sr, w, codes, &sb, &ch, err);
+        J->scales_col[c * (M / 16) + i] = sb;
+        if (J->pick_col) J->pick_col[c * (M / 16) + i] = ch;
+        for (int k = 0; k < 16; ++k) put_nibble(J->codes_col, c * (M / 2) + (i * 16 + k) / 2, k & 1, codes[k]);
+      }
+    }
+  }
+}
+
+static void* band_thread(void* arg) {
+  quantize_band((const band_job*)arg);
+  return NULL;
+}
+
+int orc_quantize(const void* x, int dtype, int64_t rows, int64_t cols, const orc_config* cfg, float amax,
+                 uint8_t* codes_row, uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
+                 float* tensor_scale, uint8_t* pick_row, uint8_t* pick_col, int nthreads) {
+  if (rows < 0 || cols < 0) return 1;
+  if (dtype != ORC_IN_BF16 && dtype != ORC_IN_F32) return 1;
+  if (cfg->cap != 448.0f && cfg->cap != 256.0f) return 1;
+  if (cfg->rule < ORC_RULE_NONE || cfg->rule > ORC_RULE_MAXERR) return 1;
+  if (cols % 16) return 1;
+  int need16 = cfg->block_2d || cfg->emit_col;
+  if (need16 && rows % 16) return 1;
+  if (cfg->rht && (cfg->block_2d || cfg->emit_col)) return 1;
+  float s_t = orc_tensor_scale(amax, cfg->cap);
+  if (tensor_scale) *tensor_scale = s_t;
+  if (rows == 0 || cols == 0) return 0;
+
+  if (nthreads < 1) nthreads = 1;
+  int64_t groups = (rows + 15) / 16; /* bands are whole 16-row groups */
+  if (nthreads > groups) nthreads = (int)groups;
+  band_job* jobs = (band_job*)calloc((size_t)nthreads, sizeof(band_job));
+  pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  if (!jobs || !th) {
+    free(jobs);
+    free(th);
+    return 2;
+  }
+  for (int t = 0; t < nthreads; ++t) {
+    int64_t g0 = groups * t / nthreads, g1 = groups * (t + 1) / nthreads;
+    band_job J = {x, dtype, rows, cols, g0 * 16, g1 * 16 < rows ? g1 * 16 : rows, cfg, s_t,
+                  codes_row, scales_row, codes_col, scales_col, pick_row, pick_col};
+    jobs[t] = J;
+  }
+  if (nthreads == 1) {
+    quantize_band(&jobs[0]);
+  } else {
+    for (int t = 0; t < nthreads; ++t) pthread_create(&th[t], NULL, band_thread, &jobs[t]);
+    for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+  }
+  free(jobs);
+  free(th);
+  return 0;
+}
+
+/* x_hat = fl(value(code) * fl(dec(sb) * S_t)): the same d as the block's
+ * chosen candidate, so this reproduces xh_i of the 4/6 error exactly. */
+void orc_dequantize(const uint8_t* codes, const uint8_t* scales, float tensor_scale, int64_t rows, int64_t cols,
+                    int block_2d, float* out) {
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t c = 0; c < cols; ++c) {
+      uint8_t byte = codes[r * (cols / 2) + c / 2];
+      uint8_t code = (c & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+      uint8_t sb = block_2d ? scales[(r / 16) * (cols / 16) + c / 16] : scales[r * (cols / 16) + c / 16];
+      float d = orc_e4m3_value(sb) * tensor_scale;
+      out[r * cols + c] = orc_e2m1_value(code) * d;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Batch wrappers (so the pins can sweep millions of values cheaply)          */
+/* ------------------------------------------------------------------------ */
+void orc_e2m1_rne_n(const float* z, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e2m1_rne(z[i]);
+}
+void orc_e2m1_sr_n(const float* z, const uint32_t* w, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e2m1_sr(z[i], w[i]);
+}
+void orc_e4m3_rne_sat_n(const float* r, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_rne_sat(r[i]);
+}
+void orc_sr_words_n(uint64_t seed, const uint64_t* idx, int64_t n, uint32_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_sr_word(seed, idx[i]);
+}
+void orc_philox_n(const uint32_t* ctr, const uint32_t* key, int64_t n, uint32_t* out) {
+  for (int64_t i = 0; i < n; ++i) orc_philox4x32_10(ctr + 4 * i, key + 2 * i, out + 4 * i);
+}
