@@ -1,0 +1,162 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 block-quantization library
+ * (libnvfp4.so).
+ *
+ * NVFP4 stores a tensor as 4-bit E2M1 codes (grid {0, 0.5, 1, 1.5, 2, 3, 4, 6},
+ * sign bit 3), one E4M3 scale per 16-element block (or per 16x16 tile) and one
+ * FP32 tensor scale.  Sources, cited by page title and section:
+ *   [P1] "Pretraining Large Language Models with NVFP4" (explainer page):
+ *        section 1 (16-element blocks with E4M3 scales), 2b (random Hadamard
+ *        transform for gradients), 2c (2D block scaling keeps the row-wise and
+ *        column-wise copies consistent), 2d (stochastic rounding).
+ *   [P2] "Technical summary: Four Over Six (4/6)": "Problem statement" (E2M1
+ *        grid; block max scaled to 6), "Core mechanism" (selected blocks scaled
+ *        to 4), "Adaptive block scaling algorithm" (quantize with both scales,
+ *        measure the error against the original values, keep the smaller under
+ *        a max-error, MAE or MSE rule), "Implementation details" (tensor scale
+ *        computed against an E4M3 limit of 256 instead of 448).
+ *
+ * Conventions for every entry point:
+ *   - Tensors are row-major rows x cols (cols contiguous).  All data pointers
+ *     are DEVICE pointers owned by the caller; the library allocates nothing
+ *     and keeps no mutable global state.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously on it; results are ready when the stream
+ *     is synchronised.
+ *   - Arguments are validated on the host before anything is launched: a
+ *     non-OK status means nothing was enqueued.  NVFP4_ERR_HIP reports a launch
+ *     failure (hipGetLastError).
+ *   - Inputs must be finite.  Non-finite inputs give unspecified codes.
+ *   - Arithmetic is IEEE binary32 with round-to-nearest-even per operation in
+ *     a fixed order, so results are bit-reproducible run to run.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_ABI_VERSION 1
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = 1,        /* a required pointer is NULL */
+  NVFP4_ERR_SHAPE = 2,       /* negative dims, or a dim not a multiple of 16 where blocks need it */
+  NVFP4_ERR_ALIGN = 3,       /* a tensor pointer is not 16-byte aligned */
+  NVFP4_ERR_DTYPE = 4,       /* unknown input dtype */
+  NVFP4_ERR_UNSUPPORTED = 5, /* invalid option combination or value */
+  NVFP4_ERR_WORKSPACE = 6,   /* workspace missing or too small */
+  NVFP4_ERR_HIP = 7          /* a HIP launch failed */
+} nvfp4_status;
+
+typedef enum { NVFP4_IN_BF16 = 0, NVFP4_IN_F32 = 1 } nvfp4_dtype;
+
+/* [P1] section 1 (1x16 blocks) and section 2c (16x16 tiles, one scale per tile). */
+typedef enum { NVFP4_BLOCK_1D = 0, NVFP4_BLOCK_2D = 1 } nvfp4_block;
+
+/* [P2] "Adaptive block scaling algorithm", step 3: the selection rules. */
+typedef enum {
+  NVFP4_RULE_NONE = 0,   /* standard NVFP4: every block's max is scaled to 6 */
+  NVFP4_RULE_MSE = 1,    /* keep the candidate with the smaller sum of squared errors */
+  NVFP4_RULE_MAE = 2,    /* ... smaller sum of absolute errors */
+  NVFP4_RULE_MAXERR = 3  /* ... smaller maximum absolute error */
+} nvfp4_rule;
+
+typedef struct {
+  int32_t block;          /* nvfp4_block */
+  int32_t emit_rowwise;   /* write the row-wise copy (blocks along cols) */
+  int32_t emit_colwise;   /* write the column-wise copy, laid out as the transpose */
+  int32_t rht;            /* 16-point random Hadamard transform on each 1x16 row block
+                             before quantization ([P1] 2b); row-wise 1D only */
+  uint32_t rht_sign_mask; /* bit i set: element i of each block is negated before the transform */
+  int32_t sr;             /* 1: stochastic rounding ([P1] 2d); 0: round to nearest even */
+  uint64_t sr_seed;       /* Philox-4x32-10 key for stochastic rounding */
+  int64_t row_offset;     /* global row of row 0: element (r, c) has index (row_offset + r) * cols + c,
+                             which keys its random word; 0 for an unsharded tensor */
+  int32_t rule;           /* nvfp4_rule: the Four Over Six choice ([P2]) */
+  float scale_cap;        /* E4M3 limit for the tensor scale: 448 (standard) or 256 ([P2]
+                             "Implementation details": leaves room for the 1.5x larger
+                             factor of a block scaled to 4) */
+} nvfp4_config;
+
+/* Device output buffers for nvfp4_quantize.  A copy not requested may be NULL.
+ *   codes_row   [rows][cols/2]      two codes per byte: element 2k in bits 0-3, 2k+1 in bits 4-7
+ *   scales_row  [rows][cols/16]     E4M3 block scales (2D: [rows/16][cols/16], one per tile)
+ *   codes_col   [cols][rows/2]      the column-wise copy: codes of x^T in the same packing
+ *   scales_col  [cols][rows/16]     (2D: [cols/16][rows/16], the transposed tile grid)
+ *   tensor_scale                    one float: S_t = amax / (6 * scale_cap)
+ * codes_* must be 16-byte aligned; scales_* and tensor_scale need natural alignment only. */
+typedef struct {
+  uint8_t* codes_row;
+  uint8_t* scales_row;
+  uint8_t* codes_col;
+  uint8_t* scales_col;
+  float* tensor_scale;
+} nvfp4_outputs;
+
+/* Bytes of device workspace nvfp4_amax needs for this shape (a few KB). */
+size_t nvfp4_amax_workspace_bytes(int64_t rows, int64_t cols);
+
+/* Per-tensor amax: *amax_dev = max |y| over the tensor, y = x, or y = the
+ * Hadamard-transformed row blocks when cfg->rht is set (the tensor scale must
+ * cover the values actually quantized).  [P2] "Implementation details" (the
+ * FP32 tensor scale is derived from it).
+ *   x          device, 16-byte aligned, rows x cols of `dtype`
+ *   cfg        host pointer; only rht and rht_sign_mask are read (NULL = no transform)
+ *   amax_dev   device, one float, written
+ *   workspace  device, at least nvfp4_amax_workspace_bytes(rows, cols) bytes, any contents
+ * An empty tensor (rows or cols == 0) gives amax 0.  With rht, cols % 16 == 0. */
+nvfp4_status nvfp4_amax(const void* x, nvfp4_dtype dtype, int64_t rows, int64_t cols, const nvfp4_config* cfg,
+                        float* amax_dev, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Quantize x into NVFP4 with one fused pass over the input.
+ * Per block (1x16 row block, 16x1 column block, or 16x16 tile):
+ *   S_t = fl(amax / fl(6 * scale_cap))
+ *   candidate T in {6} (plus {4} when rule != NONE, [P2] "Adaptive block scaling" step 1):
+ *     r = fl(m_b / fl(T * S_t)) with m_b = max |y| over the block (0 if m_b or the divisor is 0)
+ *     sb = E4M3 round-to-nearest-even of r, saturating at 448
+ *     d = fl(dec(sb) * S_t);  e = fl(1 / d) (0 when d = 0 or 1/d overflows)
+ *     code_i = E2M1 rounding of fl(y_i * e): nearest, ties to even (sr = 0), or
+ *              stochastic with the element's Philox word (sr = 1)
+ *   with a rule, the error of each candidate against y ([P2] step 2) is
+ *     eps_i = fl(y_i - fl(value(code_i) * d)); MSE / MAE: pairwise sum (index order) of
+ *     eps_i^2 / |eps_i|; MAXERR: max |eps_i|.  T = 4 is kept iff its error is strictly smaller.
+ * Stochastic rounding: the element with index idx = (row_offset + r) * cols + c uses word
+ *   (idx mod 4) of Philox-4x32-10 at key (sr_seed low, high), counter (q low, q high, 0, 0),
+ *   q = idx / 4; it rounds up iff (word >> 10) + floor(f * 2^22) >= 2^22, f the fractional
+ *   distance to the next grid point.  Both copies and both candidates use the same word.
+ * Shapes: cols % 16 == 0; rows % 16 == 0 when a column copy or 2D tiles are requested.
+ * Unsupported (NVFP4_ERR_UNSUPPORTED): rht with 2D or with a column copy; scale_cap other than
+ * 448 or 256; no copy requested; an unknown rule or block kind.
+ *   x          device, 16-byte aligned
+ *   cfg        host pointer
+ *   amax_dev   device, one float (e.g. from nvfp4_amax, or a caller-provided amax)
+ *   out        host pointer to device buffers (see nvfp4_outputs) */
+nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dtype, int64_t rows, int64_t cols, const nvfp4_config* cfg,
+                            const float* amax_dev, const nvfp4_outputs* out, void* stream);
+
+/* out[r][c] = fl(value(code) * fl(dec(sb) * S_t)), the same value the 4/6 error used.
+ *   codes        device [rows][cols/2], 16-byte aligned
+ *   scales       device [rows][cols/16] (block 1D) or [rows/16][cols/16] (block 2D)
+ *   tensor_scale device, one float (S_t as written by nvfp4_quantize)
+ *   out          device float [rows][cols], 16-byte aligned
+ * A column-wise copy is dequantized by passing its own dims (rows = original cols). */
+nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale, int64_t rows,
+                              int64_t cols, nvfp4_block block, float* out, void* stream);
+
+/* Sign mask for the Hadamard transform derived from a seed: the low 16 bits of
+ * word 0 of Philox-4x32-10 at key (seed low, seed high), counter (0, 0, 0, 1)
+ * (stochastic rounding only uses counters whose last word is 0). */
+uint32_t nvfp4_rht_signs_from_seed(uint64_t seed);
+
+const char* nvfp4_status_string(nvfp4_status s);
+int nvfp4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

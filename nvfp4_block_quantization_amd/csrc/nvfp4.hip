@@ -1,0 +1,568 @@
+// nvfp4.hip -- gfx950 kernels and the C ABI (include/nvfp4.h) of libnvfp4.so.
+//
+// Kernels:
+//   amax_partial / amax_finish  per-tensor amax: grid-stride 16-byte loads, one
+//                               partial per workgroup, a one-workgroup finish
+//                               (no atomics, so the result is order-free).
+//   quant_row                   1x16 row blocks, row-wise copy only: a flat
+//                               stream of 16-element blocks, one block per lane,
+//                               optional Hadamard transform and stochastic
+//                               rounding, Four Over Six in registers.
+//   quant_tile                  64x64 tiles for the column-wise copy and 16x16
+//                               tiles: row blocks from registers, then the tile
+//                               (and its random words) staged in LDS and read
+//                               back by columns.
+//   dequant                     codes + scales + S_t -> fp32.
+#include "nvfp4_device.hpp"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "../../include/nvfp4.h"
+
+namespace nvfp4 {
+
+constexpr int kBF16 = NVFP4_IN_BF16;
+constexpr int kF32 = NVFP4_IN_F32;
+constexpr int kThreads = 256;
+
+// ---------------------------------------------------------------- params ---
+
+struct QuantParams {
+  const float* amax;
+  float cap6;        // fl(6 * scale_cap), exact for 448 and 256
+  uint32_t rht_mask;
+  uint32_t k0, k1;   // Philox key (stochastic rounding)
+  int64_t row_offset;  // global row of row 0 (tile kernel)
+  int64_t idx_base;    // row_offset * cols: element index of the first element (row kernel)
+  int emit_row, emit_col;
+  uint8_t* codes_row;
+  uint8_t* scales_row;
+  uint8_t* codes_col;
+  uint8_t* scales_col;
+  float* tensor_scale;
+};
+
+struct TensorScale {
+  float st, den6, den4;
+};
+
+// S_t = fl(amax / fl(6 * cap)); the candidates divide the block max by
+// fl(6 * S_t) and fl(4 * S_t).
+__device__ __forceinline__ TensorScale tensor_scale(const float* amax, float cap6) {
+  TensorScale t;
+  t.st = __fdiv_rn(*amax, cap6);
+  t.den6 = 6.0f * t.st;
+  t.den4 = 4.0f * t.st;
+  return t;
+}
+
+// Load 16 consecutive input elements (16-byte aligned) as binary32.
+template <int DT>
+__device__ __forceinline__ void load16(const void* __restrict__ x, int64_t elem0, float* y) {
+  if constexpr (DT == kBF16) {
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + elem0);
+    const uint4 a = p[0], b = p[1];
+    unpack_bf16x8(a, y);
+    unpack_bf16x8(b, y + 8);
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + elem0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 v = p[j];
+      y[4 * j] = v.x;
+      y[4 * j + 1] = v.y;
+      y[4 * j + 2] = v.z;
+      y[4 * j + 3] = v.w;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ amax ---
+
+__device__ __forceinline__ float block_max256(float m, float* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// Without the transform: n elements, 16-byte vectors, 4 vectors in flight per
+// thread.  With it: n / 16 blocks of 16, each transformed in registers.
+template <int DT, bool RHT>
+__global__ __launch_bounds__(kThreads) void amax_partial_kernel(const void* __restrict__ x, int64_t n,
+                                                                uint32_t mask, float* __restrict__ partials) {
+  __shared__ float red[4];
+  const int64_t tid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t nth = (int64_t)gridDim.x * kThreads;
+  float m = 0.0f;
+  if constexpr (!RHT) {
+    constexpr int VEC = DT == kBF16 ? 8 : 4;
+    const int64_t nv = n / VEC;
+    const uint4* xv = reinterpret_cast<const uint4*>(x);
+    int64_t v = tid;
+    for (; v + 3 * nth < nv; v += 4 * nth) {
+      uint4 q[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) q[u] = xv[v + u * nth];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if constexpr (DT == kBF16) {
+          float y[8];
+          unpack_bf16x8(q[u], y);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(y[i]));
+        } else {
+          m = fmaxf(m, fmaxf(fmaxf(fabsf(__uint_as_float(q[u].x)), fabsf(__uint_as_float(q[u].y))),
+                             fmaxf(fabsf(__uint_as_float(q[u].z)), fabsf(__uint_as_float(q[u].w)))));
+        }
+      }
+    }
+    for (; v < nv; v += nth) {
+      const uint4 q = xv[v];
+      if constexpr (DT == kBF16) {
+        float y[8];
+        unpack_bf16x8(q, y);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(y[i]));
+      } else {
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(__uint_as_float(q.x)), fabsf(__uint_as_float(q.y))),
+                           fmaxf(fabsf(__uint_as_float(q.z)), fabsf(__uint_as_float(q.w)))));
+      }
+    }
+    for (int64_t e = nv * VEC + tid; e < n; e += nth) {
+      float f;
+      if constexpr (DT == kBF16) f = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(x)[e] << 16);
+      else f = reinterpret_cast<const float*>(x)[e];
+      m = fmaxf(m, fabsf(f));
+    }
+  } else {
+    const int64_t nb = n / 16;
+    for (int64_t b = tid; b < nb; b += nth) {
+      float y[16];
+      load16<DT>(x, 16 * b, y);
+      rht16(y, mask);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(y[i]));
+    }
+  }
+  m = block_max256(m, red);
+  if (threadIdx.x == 0) partials[blockIdx.x] = m;
+}
+
+__global__ __launch_bounds__(kThreads) void amax_finish_kernel(const float* __restrict__ partials, int n,
+                                                               float* __restrict__ amax) {
+  __shared__ float red[4];
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < n; i += kThreads) m = fmaxf(m, partials[i]);
+  m = block_max256(m, red);
+  if (threadIdx.x == 0) amax[0] = m;
+}
+
+// ------------------------------------------------------- row-wise, 1x16 ---
+
+// One 16-element block per lane; each thread takes U blocks spaced a wave
+// apart so every load instruction of the wave covers 64 consecutive blocks.
+template <int DT, bool RHT, bool SR, int RULE, int U>
+__global__ __launch_bounds__(kThreads) void quant_row_kernel(const void* __restrict__ x, int64_t nblocks,
+                                                             QuantParams p) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t base = ((int64_t)blockIdx.x * (kThreads / 64) + wave) * (64 * U) + lane;
+  const TensorScale ts = tensor_scale(p.amax, p.cap6);
+  if (blockIdx.x == 0 && threadIdx.x == 0 && p.tensor_scale) p.tensor_scale[0] = ts.st;
+
+  float y[U][16];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t b = base + 64 * u;
+    if (b < nblocks) load16<DT>(x, 16 * b, y[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t b = base + 64 * u;
+    if (b >= nblocks) continue;
+    if constexpr (RHT) rht16(y[u], p.rht_mask);
+    uint32_t w[16];
+    if constexpr (SR) sr_words16((uint64_t)p.idx_base + (uint64_t)(16 * b), p.k0, p.k1, w);
+    const BlockResult r = quant_block16<SR, RULE>(y[u], w, ts.st, ts.den6, ts.den4);
+    *reinterpret_cast<uint2*>(p.codes_row + 8 * b) = make_uint2(r.codes.lo, r.codes.hi);
+    p.scales_row[b] = (uint8_t)r.sb;
+  }
+}
+
+// ------------------------------------------- tiles: column copy and 2D ---
+
+// A workgroup owns a 64x64 tile = 4x4 sub-blocks of 16x16; lanes 16g..16g+15
+// (one DPP row) own sub-block g, one sub-block row (row pass) or column
+// (column pass) per lane.  Consecutive workgroups on one XCD take
+// consecutive tiles, so partial output lines meet in the same L2.
+__device__ __forceinline__ int64_t xcd_tile(int64_t bid, int64_t nb) {
+  const int64_t q = nb >> 3, rem = nb & 7;
+  const int64_t xcd = bid & 7, slot = bid >> 3;
+  return xcd * q + (xcd < rem ? xcd : rem) + slot;
+}
+
+template <int DT, bool TWO_D, bool SR, int RULE>
+__global__ __launch_bounds__(kThreads) void quant_tile_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                              int64_t tiles_x, QuantParams p) {
+  constexpr int VP = DT == kBF16 ? 36 : 68;  // LDS row pitch in dwords (16 bytes of padding)
+  constexpr int WP = SR ? 68 : 1;
+  __shared__ uint32_t lds_v[64 * VP];
+  __shared__ uint32_t lds_w[SR ? 64 * WP : 1];
+
+  const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int t = threadIdx.x, g = t >> 4, i = t & 15;
+  const int bi = g >> 2, bj = g & 3;
+  const int64_t r0 = (tile / tiles_x) * 64 + 16 * bi;
+  const int64_t c0 = (tile % tiles_x) * 64 + 16 * bj;
+  const bool valid = r0 < rows && c0 < cols;  // whole 16x16 sub-blocks: rows, cols are multiples of 16
+  const TensorScale ts = tensor_scale(p.amax, p.cap6);
+  if (blockIdx.x == 0 && t == 0 && p.tensor_scale) p.tensor_scale[0] = ts.st;
+
+  // ---- row pass: lane i holds row r0 + i, columns c0 .. c0 + 15
+  float y[16];
+  uint32_t w[16];
+  uint4 raw[DT == kBF16 ? 2 : 4];
+  if (valid) {
+    const int64_t e0 = (r0 + i) * cols + c0;
+    if constexpr (DT == kBF16) {
+      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + e0);
+      raw[0] = src[0];
+      raw[1] = src[1];
+      unpack_bf16x8(raw[0], y);
+      unpack_bf16x8(raw[1], y + 8);
+    } else {
+      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(x) + e0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        raw[j] = src[j];
+        y[4 * j] = __uint_as_float(raw[j].x);
+        y[4 * j + 1] = __uint_as_float(raw[j].y);
+        y[4 * j + 2] = __uint_as_float(raw[j].z);
+        y[4 * j + 3] = __uint_as_float(raw[j].w);
+      }
+    }
+    if constexpr (SR) sr_words16((uint64_t)((p.row_offset + r0 + i) * cols + c0), p.k0, p.k1, w);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      y[k] = 0.0f;
+      w[k] = 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < (DT == kBF16 ? 2 : 4); ++j) raw[j] = make_uint4(0, 0, 0, 0);
+  }
+
+  BlockResult res;
+  if constexpr (TWO_D) res = quant_tile_row16<SR, RULE>(y, w, ts.st, ts.den6, ts.den4);
+  else res = quant_block16<SR, RULE>(y, w, ts.st, ts.den6, ts.den4);
+
+  if (valid && p.emit_row) {
+    *reinterpret_cast<uint2*>(p.codes_row + (r0 + i) * (cols / 2) + c0 / 2) = make_uint2(res.codes.lo, res.codes.hi);
+    if constexpr (TWO_D) {
+      if (i == 0) p.scales_row[(r0 / 16) * (cols / 16) + c0 / 16] = (uint8_t)res.sb;
+    } else {
+      p.scales_row[(r0 + i) * (cols / 16) + c0 / 16] = (uint8_t)res.sb;
+    }
+  }
+  if (!p.emit_col) return;  // uniform across the workgroup
+
+  // ---- stage the tile (and its random words) in LDS
+  {
+    const int row = 16 * bi + i;
+    uint4* dv = reinterpret_cast<uint4*>(lds_v + row * VP + (DT == kBF16 ? 8 : 16) * bj);
+#pragma unroll
+    for (int j = 0; j < (DT == kBF16 ? 2 : 4); ++j) dv[j] = raw[j];
+    if constexpr (SR) {
+      uint4* dw = reinterpret_cast<uint4*>(lds_w + row * WP + 16 * bj);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dw[j] = make_uint4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
+    }
+  }
+  __syncthreads();
+
+  // ---- column pass: lane i holds column c0 + i, rows r0 .. r0 + 15
+  const int col = 16 * bj + i;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int row = 16 * bi + k;
+    if constexpr (DT == kBF16) {
+      const uint16_t h = reinterpret_cast<const uint16_t*>(lds_v + row * VP)[col];
+      y[k] = __uint_as_float((uint32_t)h << 16);
+    } else {
+      y[k] = __uint_as_float(lds_v[row * VP + col]);
+    }
+    if constexpr (SR) w[k] = lds_w[row * WP + col];
+  }
+  BlockCodes cc;
+  uint32_t sbc;
+  if constexpr (TWO_D) {
+    // same values, same reciprocal, same words: the codes of the row copy, transposed
+    cc = round16<SR>(y, res.e, w);
+    sbc = res.sb;
+  } else {
+    const BlockResult rc = quant_block16<SR, RULE>(y, w, ts.st, ts.den6, ts.den4);
+    cc = rc.codes;
+    sbc = rc.sb;
+  }
+  if (valid) {
+    *reinterpret_cast<uint2*>(p.codes_col + (c0 + i) * (rows / 2) + r0 / 2) = make_uint2(cc.lo, cc.hi);
+    if constexpr (TWO_D) {
+      if (i == 0) p.scales_col[(c0 / 16) * (rows / 16) + r0 / 16] = (uint8_t)sbc;
+    } else {
+      p.scales_col[(c0 + i) * (rows / 16) + r0 / 16] = (uint8_t)sbc;
+    }
+  }
+}
+
+// Only the tensor scale (empty tensors).
+__global__ void tensor_scale_kernel(const float* __restrict__ amax, float cap6, float* __restrict__ out) {
+  if (threadIdx.x == 0) out[0] = __fdiv_rn(amax[0], cap6);
+}
+
+// ------------------------------------------------------------ dequantize ---
+
+template <bool TWO_D>
+__global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __restrict__ codes,
+                                                           const uint8_t* __restrict__ scales,
+                                                           const float* __restrict__ tsp, int64_t nblocks,
+                                                           int64_t cols, float* __restrict__ out) {
+  const float st = tsp[0];
+  const int64_t nth = (int64_t)gridDim.x * kThreads;
+  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += nth) {
+    const uint2 c = *reinterpret_cast<const uint2*>(codes + 8 * b);
+    uint32_t sb;
+    if constexpr (TWO_D) {
+      const int64_t e0 = 16 * b, r = e0 / cols, c0 = e0 - r * cols;
+      sb = scales[(r / 16) * (cols / 16) + c0 / 16];
+    } else {
+      sb = scales[b];
+    }
+    const float d = e4m3_decode(sb) * st;
+    f32x2 v[8];
+    v[0] = fp4_pair_values<0>(c.x);
+    v[1] = fp4_pair_values<1>(c.x);
+    v[2] = fp4_pair_values<2>(c.x);
+    v[3] = fp4_pair_values<3>(c.x);
+    v[4] = fp4_pair_values<0>(c.y);
+    v[5] = fp4_pair_values<1>(c.y);
+    v[6] = fp4_pair_values<2>(c.y);
+    v[7] = fp4_pair_values<3>(c.y);
+    float4* o = reinterpret_cast<float4*>(out + 16 * b);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = make_float4(v[2 * j].x * d, v[2 * j].y * d, v[2 * j + 1].x * d, v[2 * j + 1].y * d);
+  }
+}
+
+// ------------------------------------------------------------- dispatch ---
+
+template <typename F>
+static void with_bool(bool b, F&& f) {
+  if (b) f(std::true_type{});
+  else f(std::false_type{});
+}
+template <typename F>
+static void with_dtype(int dt, F&& f) {
+  if (dt == kBF16) f(std::integral_constant<int, kBF16>{});
+  else f(std::integral_constant<int, kF32>{});
+}
+template <typename F>
+static void with_rule(int rule, F&& f) {
+  switch (rule) {
+    case kRuleNone: f(std::integral_constant<int, kRuleNone>{}); break;
+    case kRuleMse: f(std::integral_constant<int, kRuleMse>{}); break;
+    case kRuleMae: f(std::integral_constant<int, kRuleMae>{}); break;
+    default: f(std::integral_constant<int, kRuleMaxErr>{}); break;
+  }
+}
+
+constexpr int kRowU = 2;
+constexpr int kAmaxMaxParts = 1024;
+
+}  // namespace nvfp4
+
+using namespace nvfp4;
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+extern "C" {
+
+int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
+
+const char* nvfp4_status_string(nvfp4_status s) {
+  switch (s) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_NULL: return "a required pointer is NULL";
+    case NVFP4_ERR_SHAPE: return "invalid shape (dims must be >= 0 and multiples of 16 where blocks need it)";
+    case NVFP4_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case NVFP4_ERR_DTYPE: return "unknown input dtype";
+    case NVFP4_ERR_UNSUPPORTED: return "unsupported option or option combination";
+    case NVFP4_ERR_WORKSPACE: return "workspace missing or too small";
+    case NVFP4_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+uint32_t nvfp4_rht_signs_from_seed(uint64_t seed) {
+  // host evaluation of Philox-4x32-10 at counter (0, 0, 0, 1)
+  uint32_t c0 = 0, c1 = 0, c2 = 0, c3 = 1, k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c0 & 0xFFFFu;
+}
+
+static int amax_parts(int64_t rows, int64_t cols) {
+  const int64_t n = rows * cols;
+  int64_t parts = (n + (int64_t)kThreads * 32 - 1) / ((int64_t)kThreads * 32);
+  if (parts < 1) parts = 1;
+  if (parts > kAmaxMaxParts) parts = kAmaxMaxParts;
+  return (int)parts;
+}
+
+size_t nvfp4_amax_workspace_bytes(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0) return 0;
+  return sizeof(float) * (size_t)amax_parts(rows, cols);
+}
+
+nvfp4_status nvfp4_amax(const void* x, nvfp4_dtype dtype, int64_t rows, int64_t cols, const nvfp4_config* cfg,
+                        float* amax_dev, void* workspace, size_t workspace_bytes, void* stream) {
+  if (rows < 0 || cols < 0) return NVFP4_ERR_SHAPE;
+  if (dtype != NVFP4_IN_BF16 && dtype != NVFP4_IN_F32) return NVFP4_ERR_DTYPE;
+  const bool rht = cfg && cfg->rht;
+  if (rht && cols % 16) return NVFP4_ERR_SHAPE;
+  if (!amax_dev) return NVFP4_ERR_NULL;
+  const int64_t n = rows * cols;
+  if (n > 0 && !x) return NVFP4_ERR_NULL;
+  if (n > 0 && !aligned16(x)) return NVFP4_ERR_ALIGN;
+  const int parts = amax_parts(rows, cols);
+  if (!workspace || workspace_bytes < sizeof(float) * (size_t)parts) return NVFP4_ERR_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  float* partials = reinterpret_cast<float*>(workspace);
+  if (n > 0) {
+    const uint32_t mask = rht ? cfg->rht_sign_mask : 0u;
+    with_dtype(dtype, [&](auto DT) {
+      with_bool(rht, [&](auto RHT) {
+        hipLaunchKernelGGL((amax_partial_kernel<DT(), RHT()>), dim3(parts), dim3(kThreads), 0, s, x, n, mask,
+                           partials);
+      });
+    });
+    hipLaunchKernelGGL(amax_finish_kernel, dim3(1), dim3(kThreads), 0, s, partials, parts, amax_dev);
+  } else {
+    hipLaunchKernelGGL(amax_finish_kernel, dim3(1), dim3(kThreads), 0, s, partials, 0, amax_dev);
+  }
+  return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dtype, int64_t rows, int64_t cols, const nvfp4_config* cfg,
+                            const float* amax_dev, const nvfp4_outputs* out, void* stream) {
+  if (!cfg || !out || !amax_dev) return NVFP4_ERR_NULL;
+  if (dtype != NVFP4_IN_BF16 && dtype != NVFP4_IN_F32) return NVFP4_ERR_DTYPE;
+  if (cfg->block != NVFP4_BLOCK_1D && cfg->block != NVFP4_BLOCK_2D) return NVFP4_ERR_UNSUPPORTED;
+  if (cfg->rule < NVFP4_RULE_NONE || cfg->rule > NVFP4_RULE_MAXERR) return NVFP4_ERR_UNSUPPORTED;
+  if (cfg->scale_cap != 448.0f && cfg->scale_cap != 256.0f) return NVFP4_ERR_UNSUPPORTED;
+  const bool two_d = cfg->block == NVFP4_BLOCK_2D;
+  const bool erow = cfg->emit_rowwise != 0, ecol = cfg->emit_colwise != 0;
+  if (!erow && !ecol) return NVFP4_ERR_UNSUPPORTED;
+  if (cfg->rht && (two_d || ecol)) return NVFP4_ERR_UNSUPPORTED;
+  if (rows < 0 || cols < 0) return NVFP4_ERR_SHAPE;
+  if (cols % 16) return NVFP4_ERR_SHAPE;
+  if ((two_d || ecol) && rows % 16) return NVFP4_ERR_SHAPE;
+  const int64_t n = rows * cols;
+  if (n > 0) {
+    if (!x) return NVFP4_ERR_NULL;
+    if (erow && (!out->codes_row || !out->scales_row)) return NVFP4_ERR_NULL;
+    if (ecol && (!out->codes_col || !out->scales_col)) return NVFP4_ERR_NULL;
+    if (!aligned16(x)) return NVFP4_ERR_ALIGN;
+    if (erow && !aligned16(out->codes_row)) return NVFP4_ERR_ALIGN;
+    if (ecol && !aligned16(out->codes_col)) return NVFP4_ERR_ALIGN;
+  }
+
+  QuantParams p;
+  p.amax = amax_dev;
+  p.cap6 = 6.0f * cfg->scale_cap;
+  p.rht_mask = cfg->rht ? (cfg->rht_sign_mask & 0xFFFFu) : 0u;
+  p.k0 = (uint32_t)cfg->sr_seed;
+  p.k1 = (uint32_t)(cfg->sr_seed >> 32);
+  p.row_offset = cfg->row_offset;
+  p.idx_base = cfg->row_offset * cols;
+  p.emit_row = erow;
+  p.emit_col = ecol;
+  p.codes_row = out->codes_row;
+  p.scales_row = out->scales_row;
+  p.codes_col = out->codes_col;
+  p.scales_col = out->scales_col;
+  p.tensor_scale = out->tensor_scale;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  if (n == 0) {
+    if (p.tensor_scale) hipLaunchKernelGGL(tensor_scale_kernel, dim3(1), dim3(64), 0, s, amax_dev, p.cap6, p.tensor_scale);
+    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+  }
+
+  if (!two_d && !ecol) {
+    const int64_t nblocks = n / 16;
+    const int64_t per_wg = (int64_t)kThreads * kRowU;
+    const int64_t grid = (nblocks + per_wg - 1) / per_wg;
+    with_dtype(dtype, [&](auto DT) {
+      with_bool(cfg->rht != 0, [&](auto RHT) {
+        with_bool(cfg->sr != 0, [&](auto SR) {
+          with_rule(cfg->rule, [&](auto RULE) {
+            hipLaunchKernelGGL((quant_row_kernel<DT(), RHT(), SR(), RULE(), kRowU>), dim3((unsigned)grid),
+                               dim3(kThreads), 0, s, x, nblocks, p);
+          });
+        });
+      });
+    });
+  } else {
+    const int64_t tiles_x = (cols + 63) / 64, tiles_y = (rows + 63) / 64;
+    const int64_t grid = tiles_x * tiles_y;
+    with_dtype(dtype, [&](auto DT) {
+      with_bool(two_d, [&](auto TWO_D) {
+        with_bool(cfg->sr != 0, [&](auto SR) {
+          with_rule(cfg->rule, [&](auto RULE) {
+            hipLaunchKernelGGL((quant_tile_kernel<DT(), TWO_D(), SR(), RULE()>), dim3((unsigned)grid),
+                               dim3(kThreads), 0, s, x, rows, cols, tiles_x, p);
+          });
+        });
+      });
+    });
+  }
+  return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale, int64_t rows,
+                              int64_t cols, nvfp4_block block, float* out, void* stream) {
+  if (block != NVFP4_BLOCK_1D && block != NVFP4_BLOCK_2D) return NVFP4_ERR_UNSUPPORTED;
+  if (rows < 0 || cols < 0 || cols % 16) return NVFP4_ERR_SHAPE;
+  if (block == NVFP4_BLOCK_2D && rows % 16) return NVFP4_ERR_SHAPE;
+  const int64_t n = rows * cols;
+  if (n == 0) return NVFP4_OK;
+  if (!codes || !scales || !tensor_scale || !out) return NVFP4_ERR_NULL;
+  if (!aligned16(codes) || !aligned16(out)) return NVFP4_ERR_ALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t nblocks = n / 16;
+  int64_t grid = (nblocks + kThreads - 1) / kThreads;
+  if (grid > 65536) grid = 65536;
+  with_bool(block == NVFP4_BLOCK_2D, [&](auto TWO_D) {
+    hipLaunchKernelGGL((dequant_kernel<TWO_D()>), dim3((unsigned)grid), dim3(kThreads), 0, s, codes, scales,
+                       tensor_scale, nblocks, cols, out);
+  });
+  return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,343 @@
+// nvfp4_device.hpp -- gfx950 device primitives for NVFP4 block quantization.
+//
+// Everything here is binary32 arithmetic with one rounding per operation; the
+// translation unit is compiled with -ffp-contract=off so that no multiply-add
+// is fused (the 4/6 error must be fl(y - fl(v * d)), two roundings).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+enum Rule : int { kRuleNone = 0, kRuleMse = 1, kRuleMae = 2, kRuleMaxErr = 3 };
+
+// ---------------------------------------------------------------- inputs ---
+
+// bf16 is the high half of a binary32 pattern: widening is a shift.
+__device__ __forceinline__ void unpack_bf16x8(const uint4 v, float* y) {
+  y[0] = __uint_as_float(v.x << 16);
+  y[1] = __uint_as_float(v.x & 0xFFFF0000u);
+  y[2] = __uint_as_float(v.y << 16);
+  y[3] = __uint_as_float(v.y & 0xFFFF0000u);
+  y[4] = __uint_as_float(v.z << 16);
+  y[5] = __uint_as_float(v.z & 0xFFFF0000u);
+  y[6] = __uint_as_float(v.w << 16);
+  y[7] = __uint_as_float(v.w & 0xFFFF0000u);
+}
+
+// ------------------------------------------------------------------ E4M3 ---
+
+// Nearest E4M3 (OCP E4M3FN: bias 7, subnormals m * 2^-9, max 448 = 0x7E),
+// ties to even mantissa, saturating: r >= 448 (and +inf) -> 0x7E.  r >= 0.
+__device__ __forceinline__ uint32_t e4m3_encode(float r) {
+  if (!(r < 448.0f)) return 0x7Eu;
+  if (r < 0.015625f) {  // below 2^-6: quantum 2^-9; r * 512 is exact, rint is nearest-even
+    return (uint32_t)__builtin_rintf(r * 512.0f);
+  }
+  const uint32_t b = __float_as_uint(r);
+  // keep 3 mantissa bits with round-to-nearest-even; a carry moves into the exponent
+  const uint32_t rounded = b + 0x7FFFFu + ((b >> 20) & 1u);
+  return (rounded >> 20) - (120u << 3);  // rebias 127 -> 7
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  return c < 8u ? (float)c * 0.001953125f : __uint_as_float((c + (120u << 3)) << 20);
+}
+
+// ------------------------------------------------------------------ E2M1 ---
+
+// Round-to-nearest-even to E2M1 of two values into byte SEL of `old`
+// (low nibble = a).  The gfx950 convert at scale 1.0 matches nearest-even with
+// saturation at 6 and a kept sign bit for every finite binary32 input.
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_rne_pair(uint32_t old, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+
+// Stochastic rounding of two values with their own random words; returns the
+// byte (low nibble = a) in bits 0-7, other bits unspecified.  The convert's
+// first slot rounds up iff (w >> 10) + floor(f * 2^22) >= 2^22; its second slot
+// reads the word one bit lower, so that word is pre-shifted to give the same
+// decision rule.  (The destination's unused bytes are not defined by the
+// builtin, hence the masks.)
+__device__ __forceinline__ uint32_t cvt_sr_pair(float a, float b, uint32_t wa, uint32_t wb) {
+  const f32x2 sa = {a, 0.0f};
+  const f32x2 sb = {0.0f, b};
+  const uint32_t lo = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, sa, wa, 1.0f, 0);
+  const uint32_t hi = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, sb, wb >> 1, 1.0f, 0);
+  return (lo & 0x0Fu) | (hi & 0xF0u);
+}
+
+// The two E2M1 values in byte SEL of a packed word (exact at scale 1.0).
+template <int SEL>
+__device__ __forceinline__ f32x2 fp4_pair_values(uint32_t packed) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, SEL);
+}
+
+// ---------------------------------------------------------------- Philox ---
+
+// Philox-4x32-10 (Salmon et al., SC'11).  Keys are wave-uniform.
+struct U4 {
+  uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ U4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                            uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return U4{c0, c1, c2, c3};
+}
+
+// Words for 16 consecutive elements starting at idx0 (idx0 % 4 == 0):
+// element idx uses word (idx mod 4) of the block at counter (idx/4, 0, 0).
+__device__ __forceinline__ void sr_words16(uint64_t idx0, uint32_t k0, uint32_t k1, uint32_t* w) {
+  const uint64_t q0 = idx0 >> 2;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint64_t q = q0 + j;
+    const U4 r = philox4x32_10((uint32_t)q, (uint32_t)(q >> 32), 0u, 0u, k0, k1);
+    w[4 * j + 0] = r.x;
+    w[4 * j + 1] = r.y;
+    w[4 * j + 2] = r.z;
+    w[4 * j + 3] = r.w;
+  }
+}
+
+// ---------------------------------------------------------- Hadamard 16 ---
+
+// y = H16 * D * x / 4: sign flips from `mask`, butterflies h = 1, 2, 4, 8 in
+// that order with (a, b) -> (a + b, a - b), then the exact scaling by 1/4.
+__device__ __forceinline__ void rht16(float* v, uint32_t mask) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = __uint_as_float(__float_as_uint(v[i]) ^ (((mask >> i) & 1u) << 31));
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i & h) continue;
+      const float a = v[i], b = v[i + h];
+      v[i] = a + b;
+      v[i + h] = a - b;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = 0.25f * v[i];
+}
+
+// --------------------------------------------------------- cross-lane ---
+
+// DPP lane exchanges inside a row of 16 lanes.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within each 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within each 16
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Max over the 16 lanes of a DPP row (exact and order-free).
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppMirror>(v));
+  return v;
+}
+
+// Pairwise sum in lane order over a 16-lane row: lanes (2k, 2k+1), then pairs
+// of pairs, ...; both partners add the same two operands, so every lane ends
+// with the identical value.
+__device__ __forceinline__ float row16_pairwise_sum(float v) {
+  v = v + dpp<kDppXor1>(v);
+  v = v + dpp<kDppXor2>(v);
+  v = v + dpp<kDppHalfMirror>(v);
+  v = v + dpp<kDppMirror>(v);
+  return v;
+}
+
+// ------------------------------------------------------- block quantize ---
+
+struct BlockCodes {
+  uint32_t lo, hi;  // 16 packed codes: element 2k in bits 4k..4k+3 of the 64-bit pair
+};
+
+// Pairwise sum of 16 values in index order.
+__device__ __forceinline__ float pairwise16(const float* t) {
+  float s[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s[i] = t[2 * i] + t[2 * i + 1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s[i] = s[2 * i] + s[2 * i + 1];
+  s[0] = s[0] + s[1];
+  s[1] = s[2] + s[3];
+  return s[0] + s[1];
+}
+
+// Scale and round 16 values with reciprocal e.
+template <bool SR>
+__device__ __forceinline__ BlockCodes round16(const float* y, float e, const uint32_t* w) {
+  BlockCodes c;
+  if constexpr (!SR) {
+    uint32_t lo = 0, hi = 0;
+    lo = cvt_rne_pair<0>(lo, y[0] * e, y[1] * e);
+    lo = cvt_rne_pair<1>(lo, y[2] * e, y[3] * e);
+    lo = cvt_rne_pair<2>(lo, y[4] * e, y[5] * e);
+    lo = cvt_rne_pair<3>(lo, y[6] * e, y[7] * e);
+    hi = cvt_rne_pair<0>(hi, y[8] * e, y[9] * e);
+    hi = cvt_rne_pair<1>(hi, y[10] * e, y[11] * e);
+    hi = cvt_rne_pair<2>(hi, y[12] * e, y[13] * e);
+    hi = cvt_rne_pair<3>(hi, y[14] * e, y[15] * e);
+    c.lo = lo;
+    c.hi = hi;
+  } else {
+    uint32_t b[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) b[k] = cvt_sr_pair(y[2 * k] * e, y[2 * k + 1] * e, w[2 * k], w[2 * k + 1]) & 0xFFu;
+    c.lo = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+    c.hi = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+  }
+  return c;
+}
+
+// Per-element error terms of one candidate: t_i = eps_i^2 (MSE) or |eps_i|
+// (MAE, MAXERR) with eps_i = fl(y_i - fl(value_i * d)).
+template <int RULE>
+__device__ __forceinline__ void error_terms16(const float* y, BlockCodes c, float d, float* t) {
+  f32x2 v[8];
+  v[0] = fp4_pair_values<0>(c.lo);
+  v[1] = fp4_pair_values<1>(c.lo);
+  v[2] = fp4_pair_values<2>(c.lo);
+  v[3] = fp4_pair_values<3>(c.lo);
+  v[4] = fp4_pair_values<0>(c.hi);
+  v[5] = fp4_pair_values<1>(c.hi);
+  v[6] = fp4_pair_values<2>(c.hi);
+  v[7] = fp4_pair_values<3>(c.hi);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float x0 = v[k].x * d, x1 = v[k].y * d;
+    const float e0 = y[2 * k] - x0, e1 = y[2 * k + 1] - x1;
+    if constexpr (RULE == kRuleMse) {
+      t[2 * k] = e0 * e0;
+      t[2 * k + 1] = e1 * e1;
+    } else {
+      t[2 * k] = fabsf(e0);
+      t[2 * k + 1] = fabsf(e1);
+    }
+  }
+}
+
+template <int RULE>
+__device__ __forceinline__ float reduce16(const float* t) {
+  if constexpr (RULE == kRuleMaxErr) {
+    float m = t[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) m = fmaxf(m, t[i]);
+    return m;
+  } else {
+    return pairwise16(t);
+  }
+}
+
+// Scale factors of one candidate (T = 6 or 4) from the block max.
+struct Scale {
+  uint32_t sb;  // E4M3 code
+  float d;      // fl(dec(sb) * S_t)
+  float e;      // fl(1 / d), 0 when d == 0 or 1/d overflows
+};
+
+__device__ __forceinline__ Scale block_scale(float m, float den, float st) {
+  Scale s;
+  const float r = (m == 0.0f || den == 0.0f) ? 0.0f : __fdiv_rn(m, den);
+  s.sb = e4m3_encode(r);
+  s.d = e4m3_decode(s.sb) * st;
+  float e = 0.0f;
+  if (s.d != 0.0f) {
+    e = __fdiv_rn(1.0f, s.d);
+    if (__builtin_isinf(e)) e = 0.0f;
+  }
+  s.e = e;
+  return s;
+}
+
+struct BlockResult {
+  BlockCodes codes;
+  uint32_t sb;
+  float e;  // reciprocal of the chosen candidate (reused to re-round the same values)
+};
+
+// One 16-element block held by one lane.  den6 = fl(6 * S_t), den4 = fl(4 * S_t).
+template <bool SR, int RULE>
+__device__ __forceinline__ BlockResult quant_block16(const float* y, const uint32_t* w, float st, float den6,
+                                                     float den4) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(y[i]));
+  const Scale s6 = block_scale(m, den6, st);
+  const BlockCodes c6 = round16<SR>(y, s6.e, w);
+  if constexpr (RULE == kRuleNone) {
+    return BlockResult{c6, s6.sb, s6.e};
+  } else {
+    const Scale s4 = block_scale(m, den4, st);
+    const BlockCodes c4 = round16<SR>(y, s4.e, w);
+    float t[16];
+    error_terms16<RULE>(y, c6, s6.d, t);
+    const float err6 = reduce16<RULE>(t);
+    error_terms16<RULE>(y, c4, s4.d, t);
+    const float err4 = reduce16<RULE>(t);
+    const bool pick4 = err4 < err6;  // a tie keeps the scale-to-6 block
+    return pick4 ? BlockResult{c4, s4.sb, s4.e} : BlockResult{c6, s6.sb, s6.e};
+  }
+}
+
+// A 16x16 tile spread over the 16 lanes of a DPP row, one tile row per lane.
+// The tile max and the candidates' errors are reduced across the row; the
+// error tree over the 256 values in row-major order is the in-lane pairwise
+// sum of each row followed by pairwise sums across lanes.
+template <bool SR, int RULE>
+__device__ __forceinline__ BlockResult quant_tile_row16(const float* y, const uint32_t* w, float st, float den6,
+                                                        float den4) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(y[i]));
+  m = row16_max(m);
+  const Scale s6 = block_scale(m, den6, st);
+  const BlockCodes c6 = round16<SR>(y, s6.e, w);
+  if constexpr (RULE == kRuleNone) {
+    return BlockResult{c6, s6.sb, s6.e};
+  } else {
+    const Scale s4 = block_scale(m, den4, st);
+    const BlockCodes c4 = round16<SR>(y, s4.e, w);
+    float t[16];
+    error_terms16<RULE>(y, c6, s6.d, t);
+    float err6 = reduce16<RULE>(t);
+    error_terms16<RULE>(y, c4, s4.d, t);
+    float err4 = reduce16<RULE>(t);
+    if constexpr (RULE == kRuleMaxErr) {
+      err6 = row16_max(err6);
+      err4 = row16_max(err4);
+    } else {
+      err6 = row16_pairwise_sum(err6);
+      err4 = row16_pairwise_sum(err4);
+    }
+    const bool pick4 = err4 < err6;
+    return pick4 ? BlockResult{c4, s4.sb, s4.e} : BlockResult{c6, s6.sb, s6.e};
+  }
+}
+
+}  // namespace nvfp4

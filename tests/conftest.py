@@ -22,3 +22,20 @@ def orc():
 def wl():
     import workloads
     return workloads
+
+
+def pytest_collection_modifyitems(config, items):
+    """GPU tests need a GPU; elsewhere they are skipped (never run on a CPU fallback)."""
+    gpu_items = [it for it in items if "gpu" in it.keywords]
+    if not gpu_items:
+        return
+    try:
+        import torch
+        has_gpu = torch.cuda.is_available()
+    except Exception:
+        has_gpu = False
+    if has_gpu:
+        return
+    skip = pytest.mark.skip(reason="no GPU in this environment")
+    for it in gpu_items:
+        it.add_marker(skip)

@@ -1,0 +1,89 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_block_quantization_amd as nv
+
+pytestmark = pytest.mark.skipif(not os.path.exists(nv.LIB_PATH), reason="libnvfp4.so not built")
+
+FAKE = 0x10000  # 16-byte aligned dummy device address (never dereferenced: validation fails first)
+
+
+def _declared_functions():
+    src = open(nv.HEADER_PATH).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 7
+    L = nv.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    assert nv.abi_version() == 1
+    for s in range(8):
+        assert nv.lib().nvfp4_status_string(s)
+
+
+def test_rht_mask_from_seed_matches_oracle(orc):
+    for seed in (0, 1, 7, 1234, 2 ** 40 + 3):
+        assert nv.rht_signs_from_seed(seed) == orc.rht_mask_from_seed(seed)
+
+
+def _q(rows=64, cols=64, x=FAKE, dtype=0, cfg=None, amax=FAKE, outs=None):
+    cfg = cfg or nv.make_config()
+    outs = outs or nv.Outputs(FAKE, FAKE, FAKE, FAKE, FAKE)
+    return nv.lib().nvfp4_quantize(ctypes.c_void_p(x) if x else None, dtype, rows, cols, ctypes.byref(cfg),
+                                   ctypes.c_void_p(amax) if amax else None, ctypes.byref(outs), None)
+
+
+def test_quantize_validation():
+    assert _q(cols=24) == nv.ERR_SHAPE
+    assert _q(rows=-1) == nv.ERR_SHAPE
+    assert _q(rows=8, cfg=nv.make_config(colwise=True)) == nv.ERR_SHAPE
+    assert _q(rows=8, cfg=nv.make_config(block="2d")) == nv.ERR_SHAPE
+    assert _q(cfg=nv.make_config(block="2d", rht=True)) == nv.ERR_UNSUPPORTED
+    assert _q(cfg=nv.make_config(colwise=True, rht=True)) == nv.ERR_UNSUPPORTED
+    assert _q(cfg=nv.make_config(scale_cap=300.0)) == nv.ERR_UNSUPPORTED
+    assert _q(cfg=nv.make_config(rowwise=False, colwise=False)) == nv.ERR_UNSUPPORTED
+    bad_rule = nv.make_config()
+    bad_rule.rule = 7
+    assert _q(cfg=bad_rule) == nv.ERR_UNSUPPORTED
+    assert _q(dtype=5) == nv.ERR_DTYPE
+    assert _q(x=0) == nv.ERR_NULL
+    assert _q(amax=0) == nv.ERR_NULL
+    assert _q(outs=nv.Outputs(None, FAKE, None, None, FAKE)) == nv.ERR_NULL
+    assert _q(x=FAKE + 4) == nv.ERR_ALIGN
+    assert _q(outs=nv.Outputs(FAKE + 8, FAKE, None, None, FAKE)) == nv.ERR_ALIGN
+
+
+def test_amax_and_dequantize_validation():
+    L = nv.lib()
+    cfg = nv.make_config(rht=True)
+    ws = nv.amax_workspace_bytes(64, 64)
+    assert 4 <= ws <= 4096
+    P = ctypes.c_void_p
+    assert L.nvfp4_amax(P(FAKE), 0, 64, 24, ctypes.byref(cfg), P(FAKE), P(FAKE), ws, None) == nv.ERR_SHAPE
+    assert L.nvfp4_amax(P(FAKE), 0, 64, 64, None, P(FAKE), P(FAKE), ws - 4, None) == nv.ERR_WORKSPACE
+    assert L.nvfp4_amax(P(FAKE), 0, 64, 64, None, None, P(FAKE), ws, None) == nv.ERR_NULL
+    assert L.nvfp4_amax(P(FAKE + 2), 0, 64, 64, None, P(FAKE), P(FAKE), ws, None) == nv.ERR_ALIGN
+    assert L.nvfp4_amax(P(FAKE), 3, 64, 64, None, P(FAKE), P(FAKE), ws, None) == nv.ERR_DTYPE
+    assert L.nvfp4_dequantize(P(FAKE), P(FAKE), P(FAKE), 16, 24, 0, P(FAKE), None) == nv.ERR_SHAPE
+    assert L.nvfp4_dequantize(P(FAKE), P(FAKE), P(FAKE), 8, 32, 1, P(FAKE), None) == nv.ERR_SHAPE
+    assert L.nvfp4_dequantize(P(FAKE), P(FAKE), P(FAKE), 16, 32, 2, P(FAKE), None) == nv.ERR_UNSUPPORTED
+    assert L.nvfp4_dequantize(None, P(FAKE), P(FAKE), 16, 32, 0, P(FAKE), None) == nv.ERR_NULL
+    assert L.nvfp4_dequantize(P(FAKE + 8), P(FAKE), P(FAKE), 16, 32, 0, P(FAKE), None) == nv.ERR_ALIGN
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    with pytest.raises(TypeError):
+        nv.amax(torch.zeros(16, 16, dtype=torch.bfloat16))

@@ -1,0 +1,238 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, bit for
+bit, on the same seeded inputs.  Small shapes are compared whole; the five
+full-size workloads are compared on sampled row bands (the oracle recomputes
+those bands with the full tensor's amax and their global row offset)."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+torch = pytest.importorskip("torch")
+nv = pytest.importorskip("nvfp4_block_quantization_amd")
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg: str) -> None:
+    print(f"[gpu-parity] {msg}", flush=True)
+
+
+def to_gpu(x: np.ndarray) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if x.dtype == np.uint16:
+        t = t.view(torch.bfloat16)
+    return t.cuda()
+
+
+def f32_bits(a) -> np.ndarray:
+    return np.asarray(a, np.float32).view(np.uint32)
+
+
+def gpu_quantize(xg, c, amax_t=None):
+    if amax_t is None:
+        amax_t = nv.amax(xg, rht=c["rht"], rht_mask=c.get("rht_mask", 0))
+    out = nv.quantize(xg, amax_t, block=c["block"], rowwise=c["emit_row"], colwise=c["emit_col"], rht=c["rht"],
+                      rht_mask=c.get("rht_mask", 0), sr=c["sr"], sr_seed=c["sr_seed"], rule=c["rule"],
+                      scale_cap=c["cap"], row_offset=c.get("row_offset", 0))
+    return amax_t, out
+
+
+def oracle_cfg(c, row_offset=None):
+    return oracle.make_config(block=c["block"], emit_row=c["emit_row"], emit_col=c["emit_col"], rht=c["rht"],
+                              rht_mask=c.get("rht_mask", 0), sr=c["sr"], sr_seed=c["sr_seed"],
+                              row_offset=c.get("row_offset", 0) if row_offset is None else row_offset,
+                              rule=c["rule"], cap=c["cap"])
+
+
+def with_mask(c):
+    c = dict(c)
+    c["rht_mask"] = nv.rht_signs_from_seed(c["rht_seed"]) if c["rht"] else 0
+    return c
+
+
+def compare_all(x, c, tag):
+    """Whole-tensor parity for a small case."""
+    say(f"{tag}: shape {c['rows']}x{c['cols']} block={c['block']} row={c['emit_row']} col={c['emit_col']} "
+        f"rht={c['rht']} sr={c['sr']} rule={c['rule']} cap={c['cap']}")
+    xg = to_gpu(x)
+    a_t, out = gpu_quantize(xg, c)
+    torch.cuda.synchronize()
+    A = oracle.amax(x, rht=c["rht"], mask=c.get("rht_mask", 0))
+    assert f32_bits(a_t.cpu().numpy())[0] == f32_bits(A), f"{tag}: amax"
+    ref = oracle.quantize(x, oracle_cfg(c), A)
+    assert f32_bits(out["tensor_scale"].cpu().numpy())[0] == f32_bits(ref["tensor_scale"]), f"{tag}: tensor scale"
+    for k in ("codes_row", "scales_row", "codes_col", "scales_col"):
+        if k in ref:
+            got = out[k].cpu().numpy()
+            if not np.array_equal(got, ref[k]):
+                bad = np.argwhere(got != ref[k])
+                raise AssertionError(f"{tag}: {k} differs at {len(bad)} places, first {bad[:5].tolist()}")
+    return xg, a_t, out, ref
+
+
+# ------------------------------------------------------- small, whole ----
+
+SMALL = [
+    # (workload, rows, cols): several tiles plus a ragged tail in both directions
+    (1, 256, 256),
+    (1, 33, 80),
+    (2, 272, 4112),
+    (3, 80, 336),
+    (3, 144, 208),
+    (4, 48, 1040),
+    (5, 144, 400),
+    (5, 208, 176),
+]
+
+
+@pytest.mark.parametrize("k,rows,cols", SMALL)
+def test_small_workloads_bit_exact(k, rows, cols):
+    c = with_mask(workloads.config(k, rows, cols))
+    x = workloads.inputs(c, seed=0)
+    compare_all(x, c, f"workload{k}")
+    if k == 5:
+        compare_all(x, dict(c, rule="none", cap=448.0), "workload5-plain")
+
+
+@pytest.mark.parametrize("rule", ["none", "mse", "mae", "maxerr"])
+@pytest.mark.parametrize("sr", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("path", ["row", "row+col", "col", "2d", "2d-row", "row-rht"])
+def test_option_matrix(rule, sr, dtype, path):
+    rows, cols = 80, 208
+    kind = 1 if dtype == "f32" else 5
+    x = workloads.generate(kind, rows, cols, seed=21)
+    c = dict(rows=rows, cols=cols, block="2d" if path.startswith("2d") else "1d",
+             emit_row=path != "col", emit_col=path in ("row+col", "col", "2d"), rht=path == "row-rht",
+             rht_mask=0xB3E1 if path == "row-rht" else 0, sr=sr, sr_seed=99, rule=rule,
+             cap=256.0 if rule != "none" else 448.0)
+    compare_all(x, c, f"matrix-{path}-{dtype}-{rule}-sr{int(sr)}")
+
+
+def test_row_offset_keys_the_random_stream():
+    x = workloads.generate(5, 64, 96, seed=4)
+    c = dict(rows=64, cols=96, block="1d", emit_row=True, emit_col=True, rht=False, sr=True, sr_seed=7,
+             rule="mae", cap=256.0, row_offset=4096)
+    compare_all(x, c, "row-offset")
+
+
+def test_dequantize_matches_oracle():
+    for k, rows, cols in ((1, 256, 256), (3, 80, 336), (5, 144, 400)):
+        c = workloads.config(k, rows, cols)
+        x = workloads.inputs(c)
+        xg, a_t, out, ref = compare_all(x, c, f"dequant-{k}")
+        st = ref["tensor_scale"]
+        blk = c["block"]
+        if c["emit_row"]:
+            say(f"dequantize row copy {rows}x{cols} block={blk}")
+            d = nv.dequantize(out["codes_row"], out["scales_row"], out["tensor_scale"], rows, cols, blk)
+            r = oracle.dequantize(ref["codes_row"], ref["scales_row"], st, rows, cols, blk)
+            assert np.array_equal(f32_bits(d.cpu().numpy()), f32_bits(r))
+        if c["emit_col"]:
+            say(f"dequantize col copy {cols}x{rows} block={blk}")
+            d = nv.dequantize(out["codes_col"], out["scales_col"], out["tensor_scale"], cols, rows, blk)
+            r = oracle.dequantize(ref["codes_col"], ref["scales_col"], st, cols, rows, blk)
+            assert np.array_equal(f32_bits(d.cpu().numpy()), f32_bits(r))
+            if blk == "2d":  # both orientations dequantize to the same tensor
+                d_row = nv.dequantize(out["codes_row"], out["scales_row"], out["tensor_scale"], rows, cols, blk)
+                assert torch.equal(d_row.view(torch.int32), d.t().contiguous().view(torch.int32))
+
+
+def test_edge_cases():
+    # empty tensor: amax 0, tensor scale 0
+    say("edge: empty")
+    xg = torch.empty((0, 32), dtype=torch.bfloat16, device="cuda")
+    a = nv.amax(xg)
+    out = nv.quantize(xg, a)
+    torch.cuda.synchronize()
+    assert a.item() == 0.0 and out["tensor_scale"].item() == 0.0
+    base = dict(block="1d", emit_row=True, emit_col=True, rht=False, sr=False, sr_seed=0, rule="mae", cap=256.0)
+    # zeros, signed zeros, a single nonzero, tiny (subnormal-range) and huge values
+    z = np.zeros((32, 48), np.float32)
+    compare_all(z, dict(base, rows=32, cols=48), "edge-zeros")
+    compare_all(-z, dict(base, rows=32, cols=48), "edge-negzeros")
+    one = z.copy()
+    one[5, 7] = -3.5
+    compare_all(one, dict(base, rows=32, cols=48, sr=True, sr_seed=3), "edge-single")
+    rng = np.random.default_rng(2)
+    tiny = (rng.standard_normal((32, 48)) * 1e-39).astype(np.float32)
+    compare_all(tiny, dict(base, rows=32, cols=48), "edge-tiny")
+    compare_all(tiny, dict(base, rows=32, cols=48, block="2d", rule="mse"), "edge-tiny-2d")
+    huge = (rng.standard_normal((32, 48)) * 1e37).astype(np.float32)
+    compare_all(huge, dict(base, rows=32, cols=48, sr=True, sr_seed=5), "edge-huge")
+    # a caller-provided amax smaller than the data (saturating blocks) and larger (tiny scales)
+    x = workloads.generate(5, 32, 48, seed=8)
+    xg = to_gpu(x)
+    for A in (0.5, 1e6, 3.0e-30):
+        c = dict(base, rows=32, cols=48, sr=True, sr_seed=11)
+        say(f"edge: given amax {A}")
+        a_t = torch.tensor([A], dtype=torch.float32, device="cuda")
+        _, out = gpu_quantize(xg, c, a_t)
+        ref = oracle.quantize(x, oracle_cfg(c), float(np.float32(A)))
+        for k in ("codes_row", "scales_row", "codes_col", "scales_col"):
+            assert np.array_equal(out[k].cpu().numpy(), ref[k]), (A, k)
+
+
+def test_rht_mask_derivation():
+    for seed in (0, 1234, 2 ** 33 + 5):
+        assert nv.rht_signs_from_seed(seed) == oracle.rht_mask_from_seed(seed)
+
+
+def test_invalid_arguments_raise_on_gpu():
+    xg = torch.zeros((8, 24), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(nv.NVFP4Error):
+        nv.quantize(xg, nv.amax(torch.zeros((8, 32), dtype=torch.bfloat16, device="cuda")))
+
+
+# ------------------------------------------------- full size, sampled ----
+
+def _bands(rows, n=4, h=32):
+    starts = sorted({0, rows - h, (rows // 2) // 16 * 16, (rows // 3) // 16 * 16})
+    return [(s, s + h) for s in starts[:n]]
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, "5plain"])
+def test_full_size_workloads_sampled(k):
+    c = with_mask(workloads.CONFIG5_PLAIN if k == "5plain" else workloads.CONFIGS[k])
+    rows, cols = c["rows"], c["cols"]
+    say(f"full workload {k}: generating {rows}x{cols}")
+    x = workloads.inputs(c, seed=0)
+    xg = to_gpu(x)
+    say(f"full workload {k}: GPU amax + quantize")
+    a_t, out = gpu_quantize(xg, c)
+    torch.cuda.synchronize()
+    say(f"full workload {k}: oracle amax")
+    A = oracle.amax(x, rht=c["rht"], mask=c.get("rht_mask", 0))
+    assert f32_bits(a_t.cpu().numpy())[0] == f32_bits(A)
+    st = oracle.tensor_scale(A, c["cap"])
+    assert f32_bits(out["tensor_scale"].cpu().numpy())[0] == f32_bits(st)
+    for r0, r1 in _bands(rows):
+        say(f"full workload {k}: band rows {r0}:{r1}")
+        ref = oracle.quantize(x[r0:r1], oracle_cfg(c, row_offset=r0), A)
+        if c["emit_row"]:
+            assert np.array_equal(out["codes_row"][r0:r1].cpu().numpy(), ref["codes_row"])
+            srow = out["scales_row"][r0 // 16:r1 // 16] if c["block"] == "2d" else out["scales_row"][r0:r1]
+            assert np.array_equal(srow.cpu().numpy(), ref["scales_row"])
+        if c["emit_col"]:
+            assert np.array_equal(out["codes_col"][:, r0 // 2:r1 // 2].cpu().numpy(), ref["codes_col"])
+            assert np.array_equal(out["scales_col"][:, r0 // 16:r1 // 16].cpu().numpy(), ref["scales_col"])
+    # determinism: a second run writes identical bytes
+    say(f"full workload {k}: determinism rerun")
+    _, out2 = gpu_quantize(xg, c, a_t)
+    torch.cuda.synchronize()
+    for key in ("codes_row", "scales_row", "codes_col", "scales_col"):
+        if key in out:
+            assert torch.equal(out[key], out2[key]), key
+    # properties that hold everywhere: no NaN scale code, codes cover both signs
+    for key in ("scales_row", "scales_col"):
+        if key in out:
+            assert int(out[key].max().item()) <= 0x7E
+    if k == 1:
+        say("full workload 1: dequantize")
+        d = nv.dequantize(out["codes_row"], out["scales_row"], out["tensor_scale"], rows, cols)
+        ref = oracle.quantize(x, oracle_cfg(c), A)
+        r = oracle.dequantize(ref["codes_row"], ref["scales_row"], ref["tensor_scale"], rows, cols)
+        assert np.array_equal(f32_bits(d.cpu().numpy()), f32_bits(r))
+    del xg, out, out2
+    torch.cuda.empty_cache()
