@@ -20,7 +20,7 @@
 
 #include <type_traits>
 
-#include "../../include/nvfp4.h"
+#include "nvfp4.h"
 
 namespace nvfp4 {
 
@@ -48,6 +48,14 @@ struct QuantParams {
 struct TensorScale {
   float st, den6, den4;
 };
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming load of input read exactly once.
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // S_t = fl(amax / fl(6 * cap)); the candidates divide the block max by
 // fl(6 * S_t) and fl(4 * S_t).
@@ -91,8 +99,27 @@ __device__ __forceinline__ float block_max256(float m, float* red) {
   return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-// Without the transform: n elements, 16-byte vectors, 4 vectors in flight per
-// thread.  With it: n / 16 blocks of 16, each transformed in registers.
+template <int DT>
+__device__ __forceinline__ float vec_absmax(uint4 q) {
+  if constexpr (DT == kBF16) {
+    // |bf16| as the high half of a binary32 with the sign bit cleared
+    const float a = fmaxf(__uint_as_float((q.x << 16) & 0x7FFFFFFFu), __uint_as_float(q.x & 0x7FFF0000u));
+    const float b = fmaxf(__uint_as_float((q.y << 16) & 0x7FFFFFFFu), __uint_as_float(q.y & 0x7FFF0000u));
+    const float c = fmaxf(__uint_as_float((q.z << 16) & 0x7FFFFFFFu), __uint_as_float(q.z & 0x7FFF0000u));
+    const float d = fmaxf(__uint_as_float((q.w << 16) & 0x7FFFFFFFu), __uint_as_float(q.w & 0x7FFF0000u));
+    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+  } else {
+    return fmaxf(fmaxf(fabsf(__uint_as_float(q.x)), fabsf(__uint_as_float(q.y))),
+                 fmaxf(fabsf(__uint_as_float(q.z)), fabsf(__uint_as_float(q.w))));
+  }
+}
+
+// Without the transform: n elements as 16-byte vectors; each workgroup walks
+// contiguous chunks of kThreads * kAmaxDepth vectors with kAmaxDepth loads in
+// flight per thread.  With it: n / 16
+// blocks of 16, each transformed in registers.
+constexpr int kAmaxDepth = 8;
+
 template <int DT, bool RHT>
 __global__ __launch_bounds__(kThreads) void amax_partial_kernel(const void* __restrict__ x, int64_t n,
                                                                 uint32_t mask, float* __restrict__ partials) {
@@ -104,36 +131,18 @@ __global__ __launch_bounds__(kThreads) void amax_partial_kernel(const void* __re
     constexpr int VEC = DT == kBF16 ? 8 : 4;
     const int64_t nv = n / VEC;
     const uint4* xv = reinterpret_cast<const uint4*>(x);
-    int64_t v = tid;
-    for (; v + 3 * nth < nv; v += 4 * nth) {
-      uint4 q[4];
+    // workgroup-contiguous chunks: each load instruction of a workgroup covers 4 KB
+    const int64_t chunk = (int64_t)kThreads * kAmaxDepth;
+    const int64_t nchunk = nv / chunk;
+    for (int64_t c = blockIdx.x; c < nchunk; c += gridDim.x) {
+      const uint4* base = xv + c * chunk + threadIdx.x;
+      uint4 q[kAmaxDepth];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) q[u] = xv[v + u * nth];
+      for (int u = 0; u < kAmaxDepth; ++u) q[u] = load_stream(base + u * kThreads);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if constexpr (DT == kBF16) {
-          float y[8];
-          unpack_bf16x8(q[u], y);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(y[i]));
-        } else {
-          m = fmaxf(m, fmaxf(fmaxf(fabsf(__uint_as_float(q[u].x)), fabsf(__uint_as_float(q[u].y))),
-                             fmaxf(fabsf(__uint_as_float(q[u].z)), fabsf(__uint_as_float(q[u].w)))));
-        }
-      }
+      for (int u = 0; u < kAmaxDepth; ++u) m = fmaxf(m, vec_absmax<DT>(q[u]));
     }
-    for (; v < nv; v += nth) {
-      const uint4 q = xv[v];
-      if constexpr (DT == kBF16) {
-        float y[8];
-        unpack_bf16x8(q, y);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(y[i]));
-      } else {
-        m = fmaxf(m, fmaxf(fmaxf(fabsf(__uint_as_float(q.x)), fabsf(__uint_as_float(q.y))),
-                           fmaxf(fabsf(__uint_as_float(q.z)), fabsf(__uint_as_float(q.w)))));
-      }
-    }
+    for (int64_t v = nchunk * chunk + tid; v < nv; v += nth) m = fmaxf(m, vec_absmax<DT>(xv[v]));
     for (int64_t e = nv * VEC + tid; e < n; e += nth) {
       float f;
       if constexpr (DT == kBF16) f = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(x)[e] << 16);
@@ -163,89 +172,165 @@ __global__ __launch_bounds__(kThreads) void amax_finish_kernel(const float* __re
   if (threadIdx.x == 0) amax[0] = m;
 }
 
+// Each workgroup: S_t, its (d, 1/d) table for the 127 E4M3 codes, and (block 0)
+// the tensor-scale output.
+__device__ __forceinline__ TensorScale workgroup_setup(const QuantParams& p, f32x2* tab) {
+  const TensorScale ts = tensor_scale(p.amax, p.cap6);
+  fill_scale_table(tab, ts.st);
+  if (blockIdx.x == 0 && threadIdx.x == 0 && p.tensor_scale) p.tensor_scale[0] = ts.st;
+  __syncthreads();
+  return ts;
+}
+
 // ------------------------------------------------------- row-wise, 1x16 ---
 
-// One 16-element block per lane; each thread takes U blocks spaced a wave
-// apart so every load instruction of the wave covers 64 consecutive blocks.
+// The row copy of 1x16 blocks needs no neighbour: the tensor is a flat stream
+// of 16-element blocks.  One block per lane; a chunk is U blocks per lane with
+// each wave instruction loading 64 consecutive blocks.  Persistent workgroups
+// walk the chunks and prefetch the next chunk's input while quantizing the
+// current one (ping-pong register buffers).
+template <int DT>
+struct RawBlock {
+  uint4 v[DT == kBF16 ? 2 : 4];
+};
+
+template <int DT>
+__device__ __forceinline__ void load_raw(const void* __restrict__ x, int64_t b, RawBlock<DT>& r) {
+  constexpr int NV = DT == kBF16 ? 2 : 4;
+  const uint4* src = reinterpret_cast<const uint4*>(x) + b * NV;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) r.v[j] = src[j];
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack_raw(const RawBlock<DT>& r, float* y) {
+  if constexpr (DT == kBF16) {
+    unpack_bf16x8(r.v[0], y);
+    unpack_bf16x8(r.v[1], y + 8);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      y[4 * j] = __uint_as_float(r.v[j].x);
+      y[4 * j + 1] = __uint_as_float(r.v[j].y);
+      y[4 * j + 2] = __uint_as_float(r.v[j].z);
+      y[4 * j + 3] = __uint_as_float(r.v[j].w);
+    }
+  }
+}
+
+template <int DT, bool RHT, bool SR, int RULE, int U>
+struct RowChunk {
+  RawBlock<DT> raw[U];
+
+  __device__ __forceinline__ static int64_t block(int64_t c, int u) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    return c * (kThreads * U) + (int64_t)wave * (64 * U) + 64 * u + lane;
+  }
+  __device__ __forceinline__ void load(const void* __restrict__ x, int64_t c, int64_t nblocks) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t b = block(c, u);
+      if (b < nblocks) load_raw<DT>(x, b, raw[u]);
+    }
+  }
+  __device__ __forceinline__ void process(int64_t c, int64_t nblocks, const QuantParams& p, const f32x2* tab,
+                                          const TensorScale& ts) const {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t b = block(c, u);
+      if (b >= nblocks) continue;
+      float y[16];
+      unpack_raw<DT>(raw[u], y);
+      if constexpr (RHT) rht16(y, p.rht_mask);
+      uint32_t w[16];
+      if constexpr (SR) sr_words16((uint64_t)p.idx_base + (uint64_t)(16 * b), p.k0, p.k1, w);
+      const BlockResult r = quant_block16<SR, RULE>(y, w, tab, ts.den6, ts.den4);
+      reinterpret_cast<uint2*>(p.codes_row)[b] = make_uint2(r.codes.lo, r.codes.hi);
+      p.scales_row[b] = (uint8_t)r.sb;
+    }
+  }
+};
+
 template <int DT, bool RHT, bool SR, int RULE, int U>
 __global__ __launch_bounds__(kThreads) void quant_row_kernel(const void* __restrict__ x, int64_t nblocks,
                                                              QuantParams p) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t base = ((int64_t)blockIdx.x * (kThreads / 64) + wave) * (64 * U) + lane;
-  const TensorScale ts = tensor_scale(p.amax, p.cap6);
-  if (blockIdx.x == 0 && threadIdx.x == 0 && p.tensor_scale) p.tensor_scale[0] = ts.st;
-
-  float y[U][16];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int64_t b = base + 64 * u;
-    if (b < nblocks) load16<DT>(x, 16 * b, y[u]);
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int64_t b = base + 64 * u;
-    if (b >= nblocks) continue;
-    if constexpr (RHT) rht16(y[u], p.rht_mask);
-    uint32_t w[16];
-    if constexpr (SR) sr_words16((uint64_t)p.idx_base + (uint64_t)(16 * b), p.k0, p.k1, w);
-    const BlockResult r = quant_block16<SR, RULE>(y[u], w, ts.st, ts.den6, ts.den4);
-    *reinterpret_cast<uint2*>(p.codes_row + 8 * b) = make_uint2(r.codes.lo, r.codes.hi);
-    p.scales_row[b] = (uint8_t)r.sb;
+  __shared__ f32x2 tab[128];
+  const TensorScale ts = workgroup_setup(p, tab);
+  const int64_t per_chunk = (int64_t)kThreads * U;
+  const int64_t nchunks = (nblocks + per_chunk - 1) / per_chunk;
+  const int64_t G = gridDim.x;
+  RowChunk<DT, RHT, SR, RULE, U> A, B;
+  int64_t c = blockIdx.x;
+  if (c < nchunks) A.load(x, c, nblocks);
+  for (; c < nchunks; c += 2 * G) {
+    if (c + G < nchunks) B.load(x, c + G, nblocks);
+    A.process(c, nblocks, p, tab, ts);
+    if (c + 2 * G < nchunks) A.load(x, c + 2 * G, nblocks);
+    if (c + G < nchunks) B.process(c + G, nblocks, p, tab, ts);
   }
 }
 
 // ------------------------------------------- tiles: column copy and 2D ---
 
 // A workgroup owns a 64x64 tile = 4x4 sub-blocks of 16x16; lanes 16g..16g+15
-// (one DPP row) own sub-block g, one sub-block row (row pass) or column
-// (column pass) per lane.  Consecutive workgroups on one XCD take
-// consecutive tiles, so partial output lines meet in the same L2.
-__device__ __forceinline__ int64_t xcd_tile(int64_t bid, int64_t nb) {
-  const int64_t q = nb >> 3, rem = nb & 7;
-  const int64_t xcd = bid & 7, slot = bid >> 3;
+// (one DPP row) own sub-block g: one sub-block row per lane in the row pass,
+// one sub-block column per lane in the column pass.
+//
+// Tile order: a 128-byte line of a code matrix covers 256 elements along its
+// row, i.e. four tiles: four horizontal neighbours for the row copy, four
+// vertical neighbours for the column copy.  Tiles are therefore enumerated in
+// 4x4 super-tiles (256x256 elements), and workgroups are dispatched
+// round-robin over the 8 XCDs while each XCD walks one contiguous range of
+// that order: the workgroups writing one output line run back to back on the
+// same XCD and their partial lines meet in its L2.
+__device__ __forceinline__ uint32_t xcd_tile(uint32_t bid, uint32_t nb) {
+  const uint32_t q = nb >> 3, rem = nb & 7;
+  const uint32_t xcd = bid & 7, slot = bid >> 3;
   return xcd * q + (xcd < rem ? xcd : rem) + slot;
+}
+
+// Position of tile T in the super-tile order over a grid of supers_x
+// super-tiles per band (the grid is padded to whole super-tiles).
+__device__ __forceinline__ void supertile_coords(uint32_t T, uint32_t supers_x, uint32_t& ty, uint32_t& tx) {
+  const uint32_t st = T >> 4, within = T & 15;
+  const uint32_t sty = st / supers_x, stx = st - sty * supers_x;
+  ty = sty * 4 + (within >> 2);
+  tx = stx * 4 + (within & 3);
 }
 
 template <int DT, bool TWO_D, bool SR, int RULE>
 __global__ __launch_bounds__(kThreads) void quant_tile_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
-                                                              int64_t tiles_x, QuantParams p) {
-  constexpr int VP = DT == kBF16 ? 36 : 68;  // LDS row pitch in dwords (16 bytes of padding)
+                                                              uint32_t supers_x, QuantParams p) {
+  constexpr int VP = 68;  // LDS row pitch in dwords: 64 values + 16 bytes of padding
   constexpr int WP = SR ? 68 : 1;
-  __shared__ uint32_t lds_v[64 * VP];
+  __shared__ f32x2 tab[128];
+  __shared__ float lds_v[64 * VP];
   __shared__ uint32_t lds_w[SR ? 64 * WP : 1];
 
-  const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
+  uint32_t ty, tx;
+  supertile_coords(xcd_tile(blockIdx.x, gridDim.x), supers_x, ty, tx);
+  if ((int64_t)ty * 64 >= rows || (int64_t)tx * 64 >= cols) return;  // padding tile (uniform per workgroup)
   const int t = threadIdx.x, g = t >> 4, i = t & 15;
   const int bi = g >> 2, bj = g & 3;
-  const int64_t r0 = (tile / tiles_x) * 64 + 16 * bi;
-  const int64_t c0 = (tile % tiles_x) * 64 + 16 * bj;
+  const int64_t r0 = (int64_t)ty * 64 + 16 * bi;
+  const int64_t c0 = (int64_t)tx * 64 + 16 * bj;
   const bool valid = r0 < rows && c0 < cols;  // whole 16x16 sub-blocks: rows, cols are multiples of 16
-  const TensorScale ts = tensor_scale(p.amax, p.cap6);
-  if (blockIdx.x == 0 && t == 0 && p.tensor_scale) p.tensor_scale[0] = ts.st;
+
+  // issue the input loads before the per-workgroup setup
+  RawBlock<DT> raw;
+  if (valid) {
+    constexpr int NV = DT == kBF16 ? 2 : 4;
+    const uint4* src = reinterpret_cast<const uint4*>(x) + (((r0 + i) * cols + c0) / (DT == kBF16 ? 8 : 4));
+#pragma unroll
+    for (int j = 0; j < NV; ++j) raw.v[j] = src[j];
+  }
+  const TensorScale ts = workgroup_setup(p, tab);
 
   // ---- row pass: lane i holds row r0 + i, columns c0 .. c0 + 15
   float y[16];
   uint32_t w[16];
-  uint4 raw[DT == kBF16 ? 2 : 4];
   if (valid) {
-    const int64_t e0 = (r0 + i) * cols + c0;
-    if constexpr (DT == kBF16) {
-      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + e0);
-      raw[0] = src[0];
-      raw[1] = src[1];
-      unpack_bf16x8(raw[0], y);
-      unpack_bf16x8(raw[1], y + 8);
-    } else {
-      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(x) + e0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        raw[j] = src[j];
-        y[4 * j] = __uint_as_float(raw[j].x);
-        y[4 * j + 1] = __uint_as_float(raw[j].y);
-        y[4 * j + 2] = __uint_as_float(raw[j].z);
-        y[4 * j + 3] = __uint_as_float(raw[j].w);
-      }
-    }
+    unpack_raw<DT>(raw, y);
     if constexpr (SR) sr_words16((uint64_t)((p.row_offset + r0 + i) * cols + c0), p.k0, p.k1, w);
   } else {
 #pragma unroll
@@ -253,13 +338,10 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(const void* __rest
       y[k] = 0.0f;
       w[k] = 0u;
     }
-#pragma unroll
-    for (int j = 0; j < (DT == kBF16 ? 2 : 4); ++j) raw[j] = make_uint4(0, 0, 0, 0);
   }
-
   BlockResult res;
-  if constexpr (TWO_D) res = quant_tile_row16<SR, RULE>(y, w, ts.st, ts.den6, ts.den4);
-  else res = quant_block16<SR, RULE>(y, w, ts.st, ts.den6, ts.den4);
+  if constexpr (TWO_D) res = quant_tile_row16<SR, RULE>(y, w, tab, ts.den6, ts.den4);
+  else res = quant_block16<SR, RULE>(y, w, tab, ts.den6, ts.den4);
 
   if (valid && p.emit_row) {
     *reinterpret_cast<uint2*>(p.codes_row + (r0 + i) * (cols / 2) + c0 / 2) = make_uint2(res.codes.lo, res.codes.hi);
@@ -271,12 +353,12 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(const void* __rest
   }
   if (!p.emit_col) return;  // uniform across the workgroup
 
-  // ---- stage the tile (and its random words) in LDS
+  // ---- stage the tile (and its random words) in LDS as binary32
   {
     const int row = 16 * bi + i;
-    uint4* dv = reinterpret_cast<uint4*>(lds_v + row * VP + (DT == kBF16 ? 8 : 16) * bj);
+    float4* dv = reinterpret_cast<float4*>(lds_v + row * VP + 16 * bj);
 #pragma unroll
-    for (int j = 0; j < (DT == kBF16 ? 2 : 4); ++j) dv[j] = raw[j];
+    for (int j = 0; j < 4; ++j) dv[j] = make_float4(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]);
     if constexpr (SR) {
       uint4* dw = reinterpret_cast<uint4*>(lds_w + row * WP + 16 * bj);
 #pragma unroll
@@ -290,22 +372,21 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(const void* __rest
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     const int row = 16 * bi + k;
-    if constexpr (DT == kBF16) {
-      const uint16_t h = reinterpret_cast<const uint16_t*>(lds_v + row * VP)[col];
-      y[k] = __uint_as_float((uint32_t)h << 16);
-    } else {
-      y[k] = __uint_as_float(lds_v[row * VP + col]);
-    }
+    y[k] = lds_v[row * VP + col];
     if constexpr (SR) w[k] = lds_w[row * WP + col];
   }
   BlockCodes cc;
   uint32_t sbc;
   if constexpr (TWO_D) {
     // same values, same reciprocal, same words: the codes of the row copy, transposed
+    if constexpr (SR) {
+#pragma unroll
+      for (int k = 1; k < 16; k += 2) w[k] >>= 1;
+    }
     cc = round16<SR>(y, res.e, w);
     sbc = res.sb;
   } else {
-    const BlockResult rc = quant_block16<SR, RULE>(y, w, ts.st, ts.den6, ts.den4);
+    const BlockResult rc = quant_block16<SR, RULE>(y, w, tab, ts.den6, ts.den4);
     cc = rc.codes;
     sbc = rc.sb;
   }
@@ -381,8 +462,21 @@ static void with_rule(int rule, F&& f) {
   }
 }
 
-constexpr int kRowU = 2;
+constexpr int kRowU = 1;
 constexpr int kAmaxMaxParts = 1024;
+
+// Resident workgroups of a kernel on the current device (persistent grids).
+template <typename K>
+static int64_t resident_grid(K kernel, size_t dyn_lds = 0) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1024;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel), kThreads,
+                                                    dyn_lds) != hipSuccess ||
+      per_cu <= 0)
+    per_cu = 4;
+  return (int64_t)cus * per_cu;
+}
 
 }  // namespace nvfp4
 
@@ -517,26 +611,29 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dtype, int64_t rows, int6
   if (!two_d && !ecol) {
     const int64_t nblocks = n / 16;
     const int64_t per_wg = (int64_t)kThreads * kRowU;
-    const int64_t grid = (nblocks + per_wg - 1) / per_wg;
+    const int64_t nchunks = (nblocks + per_wg - 1) / per_wg;
     with_dtype(dtype, [&](auto DT) {
       with_bool(cfg->rht != 0, [&](auto RHT) {
         with_bool(cfg->sr != 0, [&](auto SR) {
           with_rule(cfg->rule, [&](auto RULE) {
-            hipLaunchKernelGGL((quant_row_kernel<DT(), RHT(), SR(), RULE(), kRowU>), dim3((unsigned)grid),
-                               dim3(kThreads), 0, s, x, nblocks, p);
+            auto k = quant_row_kernel<DT(), RHT(), SR(), RULE(), kRowU>;
+            int64_t grid = resident_grid(k);
+            if (grid > nchunks) grid = nchunks;
+            hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), 0, s, x, nblocks, p);
           });
         });
       });
     });
   } else {
-    const int64_t tiles_x = (cols + 63) / 64, tiles_y = (rows + 63) / 64;
-    const int64_t grid = tiles_x * tiles_y;
+    const int64_t supers_x = (cols + 255) / 256, supers_y = (rows + 255) / 256;
+    const int64_t ntiles = 16 * supers_x * supers_y;  // padded to whole 4x4 super-tiles
+    if (ntiles > (1ll << 24)) return NVFP4_ERR_SHAPE;  // the dispatch counts work-items in 32 bits
     with_dtype(dtype, [&](auto DT) {
       with_bool(two_d, [&](auto TWO_D) {
         with_bool(cfg->sr != 0, [&](auto SR) {
           with_rule(cfg->rule, [&](auto RULE) {
-            hipLaunchKernelGGL((quant_tile_kernel<DT(), TWO_D(), SR(), RULE()>), dim3((unsigned)grid),
-                               dim3(kThreads), 0, s, x, rows, cols, tiles_x, p);
+            hipLaunchKernelGGL((quant_tile_kernel<DT(), TWO_D(), SR(), RULE()>), dim3((unsigned)ntiles),
+                               dim3(kThreads), 0, s, x, rows, cols, (uint32_t)supers_x, p);
           });
         });
       });

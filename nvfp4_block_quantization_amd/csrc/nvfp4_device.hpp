@@ -57,18 +57,23 @@ __device__ __forceinline__ uint32_t cvt_rne_pair(uint32_t old, float a, float b)
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
 }
 
-// Stochastic rounding of two values with their own random words; returns the
-// byte (low nibble = a) in bits 0-7, other bits unspecified.  The convert's
-// first slot rounds up iff (w >> 10) + floor(f * 2^22) >= 2^22; its second slot
-// reads the word one bit lower, so that word is pre-shifted to give the same
-// decision rule.  (The destination's unused bytes are not defined by the
-// builtin, hence the masks.)
-__device__ __forceinline__ uint32_t cvt_sr_pair(float a, float b, uint32_t wa, uint32_t wb) {
-  const f32x2 sa = {a, 0.0f};
-  const f32x2 sb = {0.0f, b};
-  const uint32_t lo = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, sa, wa, 1.0f, 0);
-  const uint32_t hi = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, sb, wb >> 1, 1.0f, 0);
-  return (lo & 0x0Fu) | (hi & 0xF0u);
+// Stochastic rounding of a pair of values into byte SEL of `d`, keeping d's
+// other bytes.  The convert's first slot rounds its value up iff
+// (r >> 10) + floor(f * 2^22) >= 2^22; its second slot reads r one bit lower.
+// (Written as inline assembly because the compiler builtin does not keep the
+// destination's other bytes.)
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_sr_byte(uint32_t d, f32x2 src, uint32_t r) {
+  if constexpr (SEL == 0) {
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0" : "+v"(d) : "v"(src), "v"(r));
+  } else if constexpr (SEL == 1) {
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,0]" : "+v"(d) : "v"(src), "v"(r));
+  } else if constexpr (SEL == 2) {
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,0,1]" : "+v"(d) : "v"(src), "v"(r));
+  } else {
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,1]" : "+v"(d) : "v"(src), "v"(r));
+  }
+  return d;
 }
 
 // The two E2M1 values in byte SEL of a packed word (exact at scale 1.0).
@@ -78,6 +83,13 @@ __device__ __forceinline__ f32x2 fp4_pair_values(uint32_t packed) {
 }
 
 // ---------------------------------------------------------------- Philox ---
+
+// a ^ b ^ c in one instruction (truth table 0x96); c must be wave-uniform (the Philox key).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t d;
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(d) : "v"(a), "v"(b), "s"(c));
+  return d;
+}
 
 // Philox-4x32-10 (Salmon et al., SC'11).  Keys are wave-uniform.
 struct U4 {
@@ -90,8 +102,8 @@ __device__ __forceinline__ U4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    const uint32_t n0 = xor3((uint32_t)(p1 >> 32), c1, k0);
+    const uint32_t n2 = xor3((uint32_t)(p0 >> 32), c3, k1);
     c1 = (uint32_t)p1;
     c3 = (uint32_t)p0;
     c0 = n0;
@@ -189,7 +201,12 @@ __device__ __forceinline__ float pairwise16(const float* t) {
   return s[0] + s[1];
 }
 
-// Scale and round 16 values with reciprocal e.
+// Scale and round 16 values with reciprocal e.  For stochastic rounding `w`
+// holds the element words with the odd elements' words already shifted right
+// by one (the convert's second slot reads its random word one bit lower): the
+// even-slot converts fill one register, the odd-slot converts another, and one
+// bitfield insert takes the low nibbles of the first and the high nibbles of
+// the second.
 template <bool SR>
 __device__ __forceinline__ BlockCodes round16(const float* y, float e, const uint32_t* w) {
   BlockCodes c;
@@ -206,11 +223,28 @@ __device__ __forceinline__ BlockCodes round16(const float* y, float e, const uin
     c.lo = lo;
     c.hi = hi;
   } else {
-    uint32_t b[8];
+    f32x2 z[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) b[k] = cvt_sr_pair(y[2 * k] * e, y[2 * k + 1] * e, w[2 * k], w[2 * k + 1]) & 0xFFu;
-    c.lo = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
-    c.hi = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+    for (int k = 0; k < 8; ++k) z[k] = f32x2{y[2 * k] * e, y[2 * k + 1] * e};
+    uint32_t ev0 = 0, od0 = 0, ev1 = 0, od1 = 0;
+    ev0 = cvt_sr_byte<0>(ev0, z[0], w[0]);
+    od0 = cvt_sr_byte<0>(od0, z[0], w[1]);
+    ev0 = cvt_sr_byte<1>(ev0, z[1], w[2]);
+    od0 = cvt_sr_byte<1>(od0, z[1], w[3]);
+    ev0 = cvt_sr_byte<2>(ev0, z[2], w[4]);
+    od0 = cvt_sr_byte<2>(od0, z[2], w[5]);
+    ev0 = cvt_sr_byte<3>(ev0, z[3], w[6]);
+    od0 = cvt_sr_byte<3>(od0, z[3], w[7]);
+    ev1 = cvt_sr_byte<0>(ev1, z[4], w[8]);
+    od1 = cvt_sr_byte<0>(od1, z[4], w[9]);
+    ev1 = cvt_sr_byte<1>(ev1, z[5], w[10]);
+    od1 = cvt_sr_byte<1>(od1, z[5], w[11]);
+    ev1 = cvt_sr_byte<2>(ev1, z[6], w[12]);
+    od1 = cvt_sr_byte<2>(od1, z[6], w[13]);
+    ev1 = cvt_sr_byte<3>(ev1, z[7], w[14]);
+    od1 = cvt_sr_byte<3>(od1, z[7], w[15]);
+    c.lo = (ev0 & 0x0F0F0F0Fu) | (od0 & 0xF0F0F0F0u);
+    c.hi = (ev1 & 0x0F0F0F0Fu) | (od1 & 0xF0F0F0F0u);
   }
   return c;
 }
@@ -261,17 +295,27 @@ struct Scale {
   float e;      // fl(1 / d), 0 when d == 0 or 1/d overflows
 };
 
-__device__ __forceinline__ Scale block_scale(float m, float den, float st) {
+// d and e depend only on the E4M3 code and S_t: each workgroup tabulates them
+// once for the 127 finite codes (one correctly rounded division per entry).
+__device__ __forceinline__ void fill_scale_table(f32x2* tab, float st) {
+  if (threadIdx.x < 128) {
+    const float d = e4m3_decode(threadIdx.x) * st;
+    float e = 0.0f;
+    if (d != 0.0f) {
+      e = __fdiv_rn(1.0f, d);
+      if (__builtin_isinf(e)) e = 0.0f;
+    }
+    tab[threadIdx.x] = f32x2{d, e};
+  }
+}
+
+__device__ __forceinline__ Scale block_scale(float m, float den, const f32x2* tab) {
   Scale s;
   const float r = (m == 0.0f || den == 0.0f) ? 0.0f : __fdiv_rn(m, den);
   s.sb = e4m3_encode(r);
-  s.d = e4m3_decode(s.sb) * st;
-  float e = 0.0f;
-  if (s.d != 0.0f) {
-    e = __fdiv_rn(1.0f, s.d);
-    if (__builtin_isinf(e)) e = 0.0f;
-  }
-  s.e = e;
+  const f32x2 de = tab[s.sb];
+  s.d = de.x;
+  s.e = de.y;
   return s;
 }
 
@@ -283,18 +327,23 @@ struct BlockResult {
 
 // One 16-element block held by one lane.  den6 = fl(6 * S_t), den4 = fl(4 * S_t).
 template <bool SR, int RULE>
-__device__ __forceinline__ BlockResult quant_block16(const float* y, const uint32_t* w, float st, float den6,
-                                                     float den4) {
+__device__ __forceinline__ BlockResult quant_block16(const float* y, const uint32_t* w, const f32x2* tab,
+                                                     float den6, float den4) {
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(y[i]));
-  const Scale s6 = block_scale(m, den6, st);
-  const BlockCodes c6 = round16<SR>(y, s6.e, w);
+  uint32_t ws[16];
+  if constexpr (SR) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) ws[k] = (k & 1) ? (w[k] >> 1) : w[k];
+  }
+  const Scale s6 = block_scale(m, den6, tab);
+  const BlockCodes c6 = round16<SR>(y, s6.e, ws);
   if constexpr (RULE == kRuleNone) {
     return BlockResult{c6, s6.sb, s6.e};
   } else {
-    const Scale s4 = block_scale(m, den4, st);
-    const BlockCodes c4 = round16<SR>(y, s4.e, w);
+    const Scale s4 = block_scale(m, den4, tab);
+    const BlockCodes c4 = round16<SR>(y, s4.e, ws);
     float t[16];
     error_terms16<RULE>(y, c6, s6.d, t);
     const float err6 = reduce16<RULE>(t);
@@ -310,19 +359,24 @@ __device__ __forceinline__ BlockResult quant_block16(const float* y, const uint3
 // error tree over the 256 values in row-major order is the in-lane pairwise
 // sum of each row followed by pairwise sums across lanes.
 template <bool SR, int RULE>
-__device__ __forceinline__ BlockResult quant_tile_row16(const float* y, const uint32_t* w, float st, float den6,
-                                                        float den4) {
+__device__ __forceinline__ BlockResult quant_tile_row16(const float* y, const uint32_t* w, const f32x2* tab,
+                                                        float den6, float den4) {
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(y[i]));
   m = row16_max(m);
-  const Scale s6 = block_scale(m, den6, st);
-  const BlockCodes c6 = round16<SR>(y, s6.e, w);
+  uint32_t ws[16];
+  if constexpr (SR) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) ws[k] = (k & 1) ? (w[k] >> 1) : w[k];
+  }
+  const Scale s6 = block_scale(m, den6, tab);
+  const BlockCodes c6 = round16<SR>(y, s6.e, ws);
   if constexpr (RULE == kRuleNone) {
     return BlockResult{c6, s6.sb, s6.e};
   } else {
-    const Scale s4 = block_scale(m, den4, st);
-    const BlockCodes c4 = round16<SR>(y, s4.e, w);
+    const Scale s4 = block_scale(m, den4, tab);
+    const BlockCodes c4 = round16<SR>(y, s4.e, ws);
     float t[16];
     error_terms16<RULE>(y, c6, s6.d, t);
     float err6 = reduce16<RULE>(t);
