@@ -46,7 +46,8 @@ struct QuantParams {
 };
 
 struct TensorScale {
-  float st, den6, den4;
+  float st;
+  Divisor den6, den4;
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -62,8 +63,8 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
 __device__ __forceinline__ TensorScale tensor_scale(const float* amax, float cap6) {
   TensorScale t;
   t.st = __fdiv_rn(*amax, cap6);
-  t.den6 = 6.0f * t.st;
-  t.den4 = 4.0f * t.st;
+  t.den6 = make_divisor(6.0f * t.st);
+  t.den4 = make_divisor(4.0f * t.st);
   return t;
 }
 
@@ -316,11 +317,15 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(const void* __rest
   const int64_t c0 = (int64_t)tx * 64 + 16 * bj;
   const bool valid = r0 < rows && c0 < cols;  // whole 16x16 sub-blocks: rows, cols are multiples of 16
 
-  // issue the input loads before the per-workgroup setup
+  // Issue the input loads before the per-workgroup setup.  Lanes of a
+  // sub-block outside the tensor read the tensor's first elements instead and
+  // store nothing (a whole 16-lane row shares the sub-block, so the 2D
+  // reductions never mix the two kinds).
   RawBlock<DT> raw;
-  if (valid) {
+  {
     constexpr int NV = DT == kBF16 ? 2 : 4;
-    const uint4* src = reinterpret_cast<const uint4*>(x) + (((r0 + i) * cols + c0) / (DT == kBF16 ? 8 : 4));
+    const int64_t e0 = valid ? (r0 + i) * cols + c0 : 0;
+    const uint4* src = reinterpret_cast<const uint4*>(x) + e0 / (DT == kBF16 ? 8 : 4);
 #pragma unroll
     for (int j = 0; j < NV; ++j) raw.v[j] = src[j];
   }
@@ -329,16 +334,8 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(const void* __rest
   // ---- row pass: lane i holds row r0 + i, columns c0 .. c0 + 15
   float y[16];
   uint32_t w[16];
-  if (valid) {
-    unpack_raw<DT>(raw, y);
-    if constexpr (SR) sr_words16((uint64_t)((p.row_offset + r0 + i) * cols + c0), p.k0, p.k1, w);
-  } else {
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      y[k] = 0.0f;
-      w[k] = 0u;
-    }
-  }
+  unpack_raw<DT>(raw, y);
+  if constexpr (SR) sr_words16((uint64_t)((p.row_offset + r0 + i) * cols + c0), p.k0, p.k1, w);
   BlockResult res;
   if constexpr (TWO_D) res = quant_tile_row16<SR, RULE>(y, w, tab, ts.den6, ts.den4);
   else res = quant_block16<SR, RULE>(y, w, tab, ts.den6, ts.den4);

@@ -32,15 +32,11 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4 v, float* y) {
 
 // Nearest E4M3 (OCP E4M3FN: bias 7, subnormals m * 2^-9, max 448 = 0x7E),
 // ties to even mantissa, saturating: r >= 448 (and +inf) -> 0x7E.  r >= 0.
+// The gfx950 fp32 -> fp8 convert rounds to nearest even and equals this
+// encoding for every binary32 r in [0, 448); above 448 it does not saturate,
+// so r is clamped first (448 itself encodes as 0x7E).
 __device__ __forceinline__ uint32_t e4m3_encode(float r) {
-  if (!(r < 448.0f)) return 0x7Eu;
-  if (r < 0.015625f) {  // below 2^-6: quantum 2^-9; r * 512 is exact, rint is nearest-even
-    return (uint32_t)__builtin_rintf(r * 512.0f);
-  }
-  const uint32_t b = __float_as_uint(r);
-  // keep 3 mantissa bits with round-to-nearest-even; a carry moves into the exponent
-  const uint32_t rounded = b + 0x7FFFFu + ((b >> 20) & 1u);
-  return (rounded >> 20) - (120u << 3);  // rebias 127 -> 7
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(r, 448.0f), 0.0f, 0, false) & 0xFFu;
 }
 
 __device__ __forceinline__ float e4m3_decode(uint32_t c) {
@@ -73,6 +69,20 @@ __device__ __forceinline__ uint32_t cvt_sr_byte(uint32_t d, f32x2 src, uint32_t 
   } else {
     asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,1]" : "+v"(d) : "v"(src), "v"(r));
   }
+  return d;
+}
+
+// First convert of a chain that writes all four bytes of a register: the
+// register's previous contents do not matter, so it is an output operand.
+__device__ __forceinline__ uint32_t cvt_sr_byte0_fresh(f32x2 src, uint32_t r) {
+  uint32_t d;
+  asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0" : "=v"(d) : "v"(src), "v"(r));
+  return d;
+}
+
+__device__ __forceinline__ uint32_t cvt_rne_byte0_fresh(float a, float b) {
+  uint32_t d;
+  asm("v_cvt_scalef32_pk_fp4_f32 %0, %1, %2, 1.0" : "=v"(d) : "v"(a), "v"(b));
   return d;
 }
 
@@ -211,12 +221,12 @@ template <bool SR>
 __device__ __forceinline__ BlockCodes round16(const float* y, float e, const uint32_t* w) {
   BlockCodes c;
   if constexpr (!SR) {
-    uint32_t lo = 0, hi = 0;
-    lo = cvt_rne_pair<0>(lo, y[0] * e, y[1] * e);
+    uint32_t lo, hi;
+    lo = cvt_rne_byte0_fresh(y[0] * e, y[1] * e);
     lo = cvt_rne_pair<1>(lo, y[2] * e, y[3] * e);
     lo = cvt_rne_pair<2>(lo, y[4] * e, y[5] * e);
     lo = cvt_rne_pair<3>(lo, y[6] * e, y[7] * e);
-    hi = cvt_rne_pair<0>(hi, y[8] * e, y[9] * e);
+    hi = cvt_rne_byte0_fresh(y[8] * e, y[9] * e);
     hi = cvt_rne_pair<1>(hi, y[10] * e, y[11] * e);
     hi = cvt_rne_pair<2>(hi, y[12] * e, y[13] * e);
     hi = cvt_rne_pair<3>(hi, y[14] * e, y[15] * e);
@@ -226,17 +236,17 @@ __device__ __forceinline__ BlockCodes round16(const float* y, float e, const uin
     f32x2 z[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) z[k] = f32x2{y[2 * k] * e, y[2 * k + 1] * e};
-    uint32_t ev0 = 0, od0 = 0, ev1 = 0, od1 = 0;
-    ev0 = cvt_sr_byte<0>(ev0, z[0], w[0]);
-    od0 = cvt_sr_byte<0>(od0, z[0], w[1]);
+    uint32_t ev0, od0, ev1, od1;
+    ev0 = cvt_sr_byte0_fresh(z[0], w[0]);
+    od0 = cvt_sr_byte0_fresh(z[0], w[1]);
     ev0 = cvt_sr_byte<1>(ev0, z[1], w[2]);
     od0 = cvt_sr_byte<1>(od0, z[1], w[3]);
     ev0 = cvt_sr_byte<2>(ev0, z[2], w[4]);
     od0 = cvt_sr_byte<2>(od0, z[2], w[5]);
     ev0 = cvt_sr_byte<3>(ev0, z[3], w[6]);
     od0 = cvt_sr_byte<3>(od0, z[3], w[7]);
-    ev1 = cvt_sr_byte<0>(ev1, z[4], w[8]);
-    od1 = cvt_sr_byte<0>(od1, z[4], w[9]);
+    ev1 = cvt_sr_byte0_fresh(z[4], w[8]);
+    od1 = cvt_sr_byte0_fresh(z[4], w[9]);
     ev1 = cvt_sr_byte<1>(ev1, z[5], w[10]);
     od1 = cvt_sr_byte<1>(od1, z[5], w[11]);
     ev1 = cvt_sr_byte<2>(ev1, z[6], w[12]);
@@ -309,10 +319,43 @@ __device__ __forceinline__ void fill_scale_table(f32x2* tab, float st) {
   }
 }
 
-__device__ __forceinline__ Scale block_scale(float m, float den, const f32x2* tab) {
+// The candidates divide the block max by a workgroup-uniform divisor den.
+// With y = fl(1/den), q0 = fl(m * y) and two residual corrections
+// (r = fma(-q, den, m) is exact; q' = fma(r, y, q)) give the correctly rounded
+// quotient fl(m / den) (Markstein's theorem; also checked against the
+// correctly rounded division over every significand of 27 binades of the
+// quotient for 64 divisors).  The theorem needs normal numbers throughout, so
+// it is used only when den is in [2^-100, 2^100]; quotients of 2^20 or more
+// saturate the E4M3 scale either way.
+struct Divisor {
+  float den;   // fl(T * S_t)
+  float y;     // fl(1 / den)
+  bool fast;   // den within the range where the corrected product is exact
+};
+
+__device__ __forceinline__ Divisor make_divisor(float den) {
+  Divisor d;
+  d.den = den;
+  d.fast = den >= 0x1p-100f && den <= 0x1p100f;
+  d.y = d.fast ? __fdiv_rn(1.0f, den) : 0.0f;
+  return d;
+}
+
+__device__ __forceinline__ float divide(float m, const Divisor& d) {
+  if (d.fast) {  // uniform branch
+    const float q0 = m * d.y;
+    const float r0 = __builtin_fmaf(-q0, d.den, m);
+    const float q1 = __builtin_fmaf(r0, d.y, q0);
+    const float r1 = __builtin_fmaf(-q1, d.den, m);
+    const float q2 = __builtin_fmaf(r1, d.y, q1);
+    return q0 < 1048576.0f ? q2 : q0;
+  }
+  return (m == 0.0f || d.den == 0.0f) ? 0.0f : __fdiv_rn(m, d.den);
+}
+
+__device__ __forceinline__ Scale block_scale(float m, const Divisor& den, const f32x2* tab) {
   Scale s;
-  const float r = (m == 0.0f || den == 0.0f) ? 0.0f : __fdiv_rn(m, den);
-  s.sb = e4m3_encode(r);
+  s.sb = e4m3_encode(divide(m, den));
   const f32x2 de = tab[s.sb];
   s.d = de.x;
   s.e = de.y;
@@ -325,10 +368,10 @@ struct BlockResult {
   float e;  // reciprocal of the chosen candidate (reused to re-round the same values)
 };
 
-// One 16-element block held by one lane.  den6 = fl(6 * S_t), den4 = fl(4 * S_t).
+// One 16-element block held by one lane.  den6: fl(6 * S_t), den4: fl(4 * S_t).
 template <bool SR, int RULE>
 __device__ __forceinline__ BlockResult quant_block16(const float* y, const uint32_t* w, const f32x2* tab,
-                                                     float den6, float den4) {
+                                                     const Divisor& den6, const Divisor& den4) {
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(y[i]));
@@ -360,7 +403,7 @@ __device__ __forceinline__ BlockResult quant_block16(const float* y, const uint3
 // sum of each row followed by pairwise sums across lanes.
 template <bool SR, int RULE>
 __device__ __forceinline__ BlockResult quant_tile_row16(const float* y, const uint32_t* w, const f32x2* tab,
-                                                        float den6, float den4) {
+                                                        const Divisor& den6, const Divisor& den4) {
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(y[i]));
