@@ -8,10 +8,11 @@
 //                               stream of 16-element blocks, one block per lane,
 //                               optional Hadamard transform and stochastic
 //                               rounding, Four Over Six in registers.
-//   quant_tile                  64x64 tiles for the column-wise copy and 16x16
-//                               tiles: row blocks from registers, then the tile
-//                               (and its random words) staged in LDS and read
-//                               back by columns.
+//   quant_strip                 256x64 strips for the column-wise copy and
+//                               16x16 tiles: row blocks from registers, each
+//                               64x64 sub-tile (and its random words) staged in
+//                               LDS and read back by columns; the column copy
+//                               leaves as whole 128-byte lines.
 //   dequant                     codes + scales + S_t -> fp32.
 #include "nvfp4_device.hpp"
 
@@ -271,128 +272,174 @@ __global__ __launch_bounds__(kThreads) void quant_row_kernel(const void* __restr
   }
 }
 
-// ------------------------------------------- tiles: column copy and 2D ---
+// ------------------------------------------ strips: column copy and 2D ---
 
-// A workgroup owns a 64x64 tile = 4x4 sub-blocks of 16x16; lanes 16g..16g+15
-// (one DPP row) own sub-block g: one sub-block row per lane in the row pass,
-// one sub-block column per lane in the column pass.
-//
-// Tile order: a 128-byte line of a code matrix covers 256 elements along its
-// row, i.e. four tiles: four horizontal neighbours for the row copy, four
-// vertical neighbours for the column copy.  Tiles are therefore enumerated in
-// 4x4 super-tiles (256x256 elements), and workgroups are dispatched
-// round-robin over the 8 XCDs while each XCD walks one contiguous range of
-// that order: the workgroups writing one output line run back to back on the
-// same XCD and their partial lines meet in its L2.
-__device__ __forceinline__ uint32_t xcd_tile(uint32_t bid, uint32_t nb) {
+// A workgroup owns a strip of 256 rows x 64 columns and walks it as four
+// 64x64 sub-tiles.  In a sub-tile, lanes 16g..16g+15 (one DPP row) own the
+// 16x16 block g: one block row per lane in the row pass, one block column per
+// lane in the column pass.  The row copy is stored straight from registers.
+// The column copy of a 256-row strip is one full 128-byte line per column of
+// the output (256 rows x 4 bits), so its codes and scales are collected in LDS
+// and written at the end with 16-byte stores, 8 whole lines per wave
+// instruction.  Strips are enumerated with the column index fastest and
+// dispatched round-robin over the XCDs with one contiguous range per XCD, so
+// the four strips that share the row copy's 128-byte lines run back to back
+// on one XCD and meet in its L2.
+constexpr int kStripRows = 256;
+
+__device__ __forceinline__ uint32_t xcd_order(uint32_t bid, uint32_t nb) {
   const uint32_t q = nb >> 3, rem = nb & 7;
   const uint32_t xcd = bid & 7, slot = bid >> 3;
   return xcd * q + (xcd < rem ? xcd : rem) + slot;
 }
 
-// Position of tile T in the super-tile order over a grid of supers_x
-// super-tiles per band (the grid is padded to whole super-tiles).
-__device__ __forceinline__ void supertile_coords(uint32_t T, uint32_t supers_x, uint32_t& ty, uint32_t& tx) {
-  const uint32_t st = T >> 4, within = T & 15;
-  const uint32_t sty = st / supers_x, stx = st - sty * supers_x;
-  ty = sty * 4 + (within >> 2);
-  tx = stx * 4 + (within & 3);
-}
-
 template <int DT, bool TWO_D, bool SR, int RULE>
-__global__ __launch_bounds__(kThreads) void quant_tile_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
-                                                              uint32_t supers_x, QuantParams p) {
-  constexpr int VP = 68;  // LDS row pitch in dwords: 64 values + 16 bytes of padding
+__global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                               uint32_t strips_x, QuantParams p) {
+  constexpr int VP = 68;  // LDS pitch (dwords) of the staged sub-tile: 64 values + 16 bytes of padding
   constexpr int WP = SR ? 68 : 1;
+  constexpr int CP = 36;  // LDS pitch (dwords) of the column-copy codes: 128 bytes + 16 of padding
   __shared__ f32x2 tab[128];
   __shared__ float lds_v[64 * VP];
   __shared__ uint32_t lds_w[SR ? 64 * WP : 1];
+  __shared__ uint32_t col_codes[64 * CP];
+  __shared__ uint32_t col_scales[TWO_D ? 16 : 256];  // 1D: [64 cols][16 bytes]; 2D: [4 tile cols][16 bytes]
 
-  uint32_t ty, tx;
-  supertile_coords(xcd_tile(blockIdx.x, gridDim.x), supers_x, ty, tx);
-  if ((int64_t)ty * 64 >= rows || (int64_t)tx * 64 >= cols) return;  // padding tile (uniform per workgroup)
+  const uint32_t strip = xcd_order(blockIdx.x, gridDim.x);
+  const uint32_t sy = strip / strips_x, sx = strip - sy * strips_x;
   const int t = threadIdx.x, g = t >> 4, i = t & 15;
   const int bi = g >> 2, bj = g & 3;
-  const int64_t r0 = (int64_t)ty * 64 + 16 * bi;
-  const int64_t c0 = (int64_t)tx * 64 + 16 * bj;
-  const bool valid = r0 < rows && c0 < cols;  // whole 16x16 sub-blocks: rows, cols are multiples of 16
+  const int64_t sr0 = (int64_t)sy * kStripRows;           // first row of the strip
+  const int64_t c0 = (int64_t)sx * 64 + 16 * bj;          // first column of this lane's blocks
+  const int64_t rows_left = rows - sr0;
+  const int nsub = (int)((rows_left < kStripRows ? rows_left : kStripRows) + 63) / 64;
+  const bool col_ok = c0 < cols;
 
-  // Issue the input loads before the per-workgroup setup.  Lanes of a
-  // sub-block outside the tensor read the tensor's first elements instead and
-  // store nothing (a whole 16-lane row shares the sub-block, so the 2D
-  // reductions never mix the two kinds).
-  RawBlock<DT> raw;
-  {
-    constexpr int NV = DT == kBF16 ? 2 : 4;
-    const int64_t e0 = valid ? (r0 + i) * cols + c0 : 0;
+  // Input of sub-tile q for this lane (lanes of blocks outside the tensor read
+  // its first elements and store nothing).
+  auto load_sub = [&](int q, RawBlock<DT>& raw) {
+    const int64_t r0 = sr0 + 64 * q + 16 * bi;
+    const int64_t e0 = (col_ok && r0 < rows) ? (r0 + i) * cols + c0 : 0;
     const uint4* src = reinterpret_cast<const uint4*>(x) + e0 / (DT == kBF16 ? 8 : 4);
 #pragma unroll
-    for (int j = 0; j < NV; ++j) raw.v[j] = src[j];
-  }
+    for (int j = 0; j < (DT == kBF16 ? 2 : 4); ++j) raw.v[j] = src[j];
+  };
+  RawBlock<DT> raw, nxt;
+  load_sub(0, raw);
   const TensorScale ts = workgroup_setup(p, tab);
 
-  // ---- row pass: lane i holds row r0 + i, columns c0 .. c0 + 15
-  float y[16];
-  uint32_t w[16];
-  unpack_raw<DT>(raw, y);
-  if constexpr (SR) sr_words16((uint64_t)((p.row_offset + r0 + i) * cols + c0), p.k0, p.k1, w);
-  BlockResult res;
-  if constexpr (TWO_D) res = quant_tile_row16<SR, RULE>(y, w, tab, ts.den6, ts.den4);
-  else res = quant_block16<SR, RULE>(y, w, tab, ts.den6, ts.den4);
+  for (int q = 0; q < nsub; ++q) {  // uniform trip count
+    const int64_t r0 = sr0 + 64 * q + 16 * bi;  // first row of this lane's 16x16 block
+    const bool valid = col_ok && r0 < rows;     // whole 16x16 blocks: rows, cols are multiples of 16
+    if (q + 1 < nsub) load_sub(q + 1, nxt);    // prefetch the next sub-tile
 
-  if (valid && p.emit_row) {
-    *reinterpret_cast<uint2*>(p.codes_row + (r0 + i) * (cols / 2) + c0 / 2) = make_uint2(res.codes.lo, res.codes.hi);
+    // ---- row pass: lane i holds row r0 + i, columns c0 .. c0 + 15
+    float y[16];
+    uint32_t w[16];
+    unpack_raw<DT>(raw, y);
+    if constexpr (SR) sr_words16((uint64_t)((p.row_offset + r0 + i) * cols + c0), p.k0, p.k1, w);
+    BlockResult res;
+    if constexpr (TWO_D) res = quant_tile_row16<SR, RULE>(y, w, tab, ts.den6, ts.den4);
+    else res = quant_block16<SR, RULE>(y, w, tab, ts.den6, ts.den4);
+
+    if (valid && p.emit_row) {
+      *reinterpret_cast<uint2*>(p.codes_row + (r0 + i) * (cols / 2) + c0 / 2) = make_uint2(res.codes.lo, res.codes.hi);
+      if constexpr (TWO_D) {
+        if (i == 0) p.scales_row[(r0 / 16) * (cols / 16) + c0 / 16] = (uint8_t)res.sb;
+      } else {
+        p.scales_row[(r0 + i) * (cols / 16) + c0 / 16] = (uint8_t)res.sb;
+      }
+    }
+    if (!p.emit_col) {  // uniform across the workgroup
+      raw = nxt;
+      continue;
+    }
+
+    // ---- stage the sub-tile (and its random words) in LDS as binary32
+    {
+      const int row = 16 * bi + i;
+      float4* dv = reinterpret_cast<float4*>(lds_v + row * VP + 16 * bj);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dv[j] = make_float4(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]);
+      if constexpr (SR) {
+        uint4* dw = reinterpret_cast<uint4*>(lds_w + row * WP + 16 * bj);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dw[j] = make_uint4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
+      }
+    }
+    __syncthreads();
+
+    // ---- column pass: lane i holds column 16 * bj + i, rows r0 .. r0 + 15
+    const int col = 16 * bj + i;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int row = 16 * bi + k;
+      y[k] = lds_v[row * VP + col];
+      if constexpr (SR) w[k] = lds_w[row * WP + col];
+    }
+    __syncthreads();  // the next sub-tile overwrites the staging area
+    BlockCodes cc;
+    uint32_t sbc;
     if constexpr (TWO_D) {
-      if (i == 0) p.scales_row[(r0 / 16) * (cols / 16) + c0 / 16] = (uint8_t)res.sb;
+      // same values, same reciprocal, same words: the codes of the row copy, transposed
+      if constexpr (SR) {
+#pragma unroll
+        for (int k = 1; k < 16; k += 2) w[k] >>= 1;
+      }
+      cc = round16<SR>(y, res.e, w);
+      sbc = res.sb;
     } else {
-      p.scales_row[(r0 + i) * (cols / 16) + c0 / 16] = (uint8_t)res.sb;
+      const BlockResult rc = quant_block16<SR, RULE>(y, w, tab, ts.den6, ts.den4);
+      cc = rc.codes;
+      sbc = rc.sb;
     }
-  }
-  if (!p.emit_col) return;  // uniform across the workgroup
-
-  // ---- stage the tile (and its random words) in LDS as binary32
-  {
-    const int row = 16 * bi + i;
-    float4* dv = reinterpret_cast<float4*>(lds_v + row * VP + 16 * bj);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dv[j] = make_float4(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]);
-    if constexpr (SR) {
-      uint4* dw = reinterpret_cast<uint4*>(lds_w + row * WP + 16 * bj);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dw[j] = make_uint4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
+    // collect: column `col`, bytes 32q + 8bi .. of its 128-byte line; scale byte 4q + bi
+    *reinterpret_cast<uint2*>(col_codes + col * CP + 8 * q + 2 * bi) = make_uint2(cc.lo, cc.hi);
+    if constexpr (TWO_D) {
+      if (i == 0) reinterpret_cast<uint8_t*>(col_scales)[bj * 16 + 4 * q + bi] = (uint8_t)sbc;
+    } else {
+      reinterpret_cast<uint8_t*>(col_scales)[col * 16 + 4 * q + bi] = (uint8_t)sbc;
     }
+    raw = nxt;
   }
+  if (!p.emit_col) return;
   __syncthreads();
 
-  // ---- column pass: lane i holds column c0 + i, rows r0 .. r0 + 15
-  const int col = 16 * bj + i;
+  // ---- write the strip's column copy: per column, rows_valid / 2 code bytes
+  // and rows_valid / 16 scale bytes, contiguous in the output
+  const int rows_valid = (int)(rows_left < kStripRows ? rows_left : kStripRows);  // a multiple of 16
+  const int cbytes = rows_valid / 2;
+  const bool wide = ((rows / 2) & 15) == 0;  // every column's line starts 16-byte aligned
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int row = 16 * bi + k;
-    y[k] = lds_v[row * VP + col];
-    if constexpr (SR) w[k] = lds_w[row * WP + col];
-  }
-  BlockCodes cc;
-  uint32_t sbc;
-  if constexpr (TWO_D) {
-    // same values, same reciprocal, same words: the codes of the row copy, transposed
-    if constexpr (SR) {
-#pragma unroll
-      for (int k = 1; k < 16; k += 2) w[k] >>= 1;
-    }
-    cc = round16<SR>(y, res.e, w);
-    sbc = res.sb;
-  } else {
-    const BlockResult rc = quant_block16<SR, RULE>(y, w, tab, ts.den6, ts.den4);
-    cc = rc.codes;
-    sbc = rc.sb;
-  }
-  if (valid) {
-    *reinterpret_cast<uint2*>(p.codes_col + (c0 + i) * (rows / 2) + r0 / 2) = make_uint2(cc.lo, cc.hi);
-    if constexpr (TWO_D) {
-      if (i == 0) p.scales_col[(c0 / 16) * (rows / 16) + r0 / 16] = (uint8_t)sbc;
+  for (int j = 0; j < 2; ++j) {
+    const int k = t + kThreads * j;
+    const int colk = k >> 3, part = k & 7;
+    const int64_t c = (int64_t)sx * 64 + colk;
+    if (c >= cols || 16 * part >= cbytes) continue;
+    uint8_t* dst = p.codes_col + c * (rows / 2) + sr0 / 2 + 16 * part;
+    const uint4 v = *reinterpret_cast<const uint4*>(col_codes + colk * CP + 4 * part);
+    if (wide && 16 * part + 16 <= cbytes) {
+      *reinterpret_cast<uint4*>(dst) = v;
     } else {
-      p.scales_col[(c0 + i) * (rows / 16) + r0 / 16] = (uint8_t)sbc;
+      *reinterpret_cast<uint2*>(dst) = make_uint2(v.x, v.y);
+      if (16 * part + 16 <= cbytes) *reinterpret_cast<uint2*>(dst + 8) = make_uint2(v.z, v.w);
+    }
+  }
+  const int sbytes = rows_valid / 16;  // scale bytes per column (1D) or per tile column (2D)
+  const uint8_t* cs = reinterpret_cast<const uint8_t*>(col_scales);
+  if constexpr (TWO_D) {
+    if (t < 4 * 16) {
+      const int tc = t >> 4, j = t & 15;
+      const int64_t ctile = (int64_t)sx * 4 + tc;
+      if (ctile * 16 < cols && j < sbytes) p.scales_col[ctile * (rows / 16) + sr0 / 16 + j] = cs[tc * 16 + j];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = t + kThreads * j;  // 64 columns x 16 bytes
+      const int colk = k >> 4, b = k & 15;
+      const int64_t c = (int64_t)sx * 64 + colk;
+      if (c < cols && b < sbytes) p.scales_col[c * (rows / 16) + sr0 / 16 + b] = cs[colk * 16 + b];
     }
   }
 }
@@ -622,15 +669,15 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dtype, int64_t rows, int6
       });
     });
   } else {
-    const int64_t supers_x = (cols + 255) / 256, supers_y = (rows + 255) / 256;
-    const int64_t ntiles = 16 * supers_x * supers_y;  // padded to whole 4x4 super-tiles
-    if (ntiles > (1ll << 24)) return NVFP4_ERR_SHAPE;  // the dispatch counts work-items in 32 bits
+    const int64_t strips_x = (cols + 63) / 64, strips_y = (rows + kStripRows - 1) / kStripRows;
+    const int64_t nstrips = strips_x * strips_y;
+    if (nstrips > (1ll << 24)) return NVFP4_ERR_SHAPE;  // the dispatch counts work-items in 32 bits
     with_dtype(dtype, [&](auto DT) {
       with_bool(two_d, [&](auto TWO_D) {
         with_bool(cfg->sr != 0, [&](auto SR) {
           with_rule(cfg->rule, [&](auto RULE) {
-            hipLaunchKernelGGL((quant_tile_kernel<DT(), TWO_D(), SR(), RULE()>), dim3((unsigned)ntiles),
-                               dim3(kThreads), 0, s, x, rows, cols, (uint32_t)supers_x, p);
+            hipLaunchKernelGGL((quant_strip_kernel<DT(), TWO_D(), SR(), RULE()>), dim3((unsigned)nstrips),
+                               dim3(kThreads), 0, s, x, rows, cols, (uint32_t)strips_x, p);
           });
         });
       });
