@@ -77,6 +77,10 @@ def lib():
             "orc_e4m3_rne_sat_n": (None, [P, i64, P]),
             "orc_sr_words_n": (None, [u64, P, i64, P]),
             "orc_philox_n": (None, [P, P, i64, P]),
+            "orc_e8m0_value": (f32, [ctypes.c_uint8]),
+            "orc_mx_scale_code": (ctypes.c_uint8, [f32]),
+            "orc_mxfp4_quantize": (i32, [P, i32, i64, i64, i32, i32, i32, u64, i64, P, P, P, P]),
+            "orc_mxfp4_dequantize": (None, [P, P, i64, i64, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -233,4 +237,43 @@ def dequantize(codes: np.ndarray, scales: np.ndarray, s_t: float, rows: int, col
     scales = np.ascontiguousarray(scales, dtype=np.uint8)
     out = np.empty((rows, cols), np.float32)
     lib().orc_dequantize(_ptr(codes), _ptr(scales), s_t, rows, cols, 1 if block == "2d" else 0, _ptr(out))
+    return out
+
+
+# ---- MXFP4 -------------------------------------------------------------------
+
+def e8m0_value(code: int) -> float:
+    return float(lib().orc_e8m0_value(code))
+
+
+def mx_scale_code(block_max: float) -> int:
+    return int(lib().orc_mx_scale_code(block_max))
+
+
+def mxfp4_quantize(x: np.ndarray, emit_row: bool = True, emit_col: bool = False, sr: bool = False,
+                   sr_seed: int = 0, row_offset: int = 0) -> dict:
+    """MXFP4 row copy (codes_row [M, N/2], scales_row [M, N/32]) and/or column
+    copy (codes_col [N, M/2], scales_col [N, M/32]) as E8M0 scale codes."""
+    x = np.ascontiguousarray(x)
+    M, N = x.shape
+    out = {}
+    cr = sr_ = cc = sc = None
+    if emit_row:
+        cr = out["codes_row"] = np.zeros((M, N // 2), np.uint8)
+        sr_ = out["scales_row"] = np.zeros((M, N // 32), np.uint8)
+    if emit_col:
+        cc = out["codes_col"] = np.zeros((N, M // 2), np.uint8)
+        sc = out["scales_col"] = np.zeros((N, M // 32), np.uint8)
+    rc = lib().orc_mxfp4_quantize(_ptr(x), _dtype_code(x), M, N, int(emit_row), int(emit_col), int(sr), sr_seed,
+                                  row_offset, _ptr(cr), _ptr(sr_), _ptr(cc), _ptr(sc))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the MXFP4 shape (code {rc})")
+    return out
+
+
+def mxfp4_dequantize(codes: np.ndarray, scales: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    out = np.empty((rows, cols), np.float32)
+    lib().orc_mxfp4_dequantize(_ptr(codes), _ptr(scales), rows, cols, _ptr(out))
     return out

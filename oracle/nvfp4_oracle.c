@@ -484,6 +484,90 @@ void orc_dequantize(const uint8_t* codes, const uint8_t* scales, float tensor_sc
 }
 
 /* ------------------------------------------------------------------------ */
+/* MXFP4: 32-element blocks with power-of-two (E8M0) scales                   */
+/* ------------------------------------------------------------------------ */
+
+float orc_e8m0_value(uint8_t code) { return (float)ldexp(1.0, (int)code - 127); }
+
+/* Shared exponent of a block: floor(log2(m)) - 2, so that the block max
+ * scales into [4, 8); clamped to the E8M0 range [-127, 127]. */
+uint8_t orc_mx_scale_code(float block_max) {
+  if (block_max == 0.0f) return 0;  /* 2^-127: every element becomes +-0 */
+  int e2;
+  frexp((double)block_max, &e2); /* block_max = f * 2^e2, f in [0.5, 1) */
+  int e = (e2 - 1) - 2;
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  return (uint8_t)(e + 127);
+}
+
+/* One 32-element block: y[k] is element k, idx[k] its flat index (for the
+ * stochastic-rounding word).  Writes 16 code bytes and returns the scale code. */
+static uint8_t mx_block(const float* y, const uint64_t* idx, int sr, uint64_t sr_seed, uint8_t* codes) {
+  float m = 0.0f;
+  for (int k = 0; k < 32; ++k) {
+    float a = fabsf(y[k]);
+    if (a > m) m = a;
+  }
+  uint8_t sc = orc_mx_scale_code(m);
+  for (int k = 0; k < 32; ++k) {
+    /* y / 2^e: exact in binary64, then one rounding to binary32 (only values far
+     * below the E2M1 grid can lose bits there) */
+    float z = (float)ldexp((double)y[k], 127 - (int)sc);
+    uint8_t c = sr ? orc_e2m1_sr(z, orc_sr_word(sr_seed, idx[k])) : orc_e2m1_rne(z);
+    put_nibble(codes, k / 2, k & 1, c);
+  }
+  return sc;
+}
+
+int orc_mxfp4_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int emit_row, int emit_col, int sr,
+                       uint64_t sr_seed, int64_t row_offset, uint8_t* codes_row, uint8_t* scales_row,
+                       uint8_t* codes_col, uint8_t* scales_col) {
+  if (rows < 0 || cols < 0) return 1;
+  if (emit_row && cols % 32) return 1;
+  if (emit_col && rows % 32) return 1;
+  if (dtype != ORC_IN_BF16 && dtype != ORC_IN_F32) return 1;
+  float y[32];
+  uint64_t idx[32];
+  if (emit_row) {
+    for (int64_t r = 0; r < rows; ++r) {
+      for (int64_t j = 0; j < cols / 32; ++j) {
+        for (int k = 0; k < 32; ++k) {
+          y[k] = load_elem(x, dtype, r * cols + j * 32 + k);
+          idx[k] = (uint64_t)((row_offset + r) * cols + j * 32 + k);
+        }
+        scales_row[r * (cols / 32) + j] = mx_block(y, idx, sr, sr_seed, codes_row + r * (cols / 2) + j * 16);
+      }
+    }
+  }
+  if (emit_col) {
+    /* the column copy: blocks of 32 rows of one column; the copy is stored
+     * transposed ([cols][rows/2]), and each element keeps its own random word */
+    for (int64_t c = 0; c < cols; ++c) {
+      for (int64_t j = 0; j < rows / 32; ++j) {
+        for (int k = 0; k < 32; ++k) {
+          y[k] = load_elem(x, dtype, (j * 32 + k) * cols + c);
+          idx[k] = (uint64_t)((row_offset + j * 32 + k) * cols + c);
+        }
+        scales_col[c * (rows / 32) + j] = mx_block(y, idx, sr, sr_seed, codes_col + c * (rows / 2) + j * 16);
+      }
+    }
+  }
+  return 0;
+}
+
+void orc_mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols, float* out) {
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t c = 0; c < cols; ++c) {
+      uint8_t byte = codes[r * (cols / 2) + c / 2];
+      uint8_t code = (c & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+      uint8_t sc = scales[r * (cols / 32) + c / 32];
+      out[r * cols + c] = (float)ldexp((double)orc_e2m1_value(code), (int)sc - 127);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Batch wrappers (so the pins can sweep millions of values cheaply)          */
 /* ------------------------------------------------------------------------ */
 void orc_e2m1_rne_n(const float* z, int64_t n, uint8_t* out) {

@@ -18,6 +18,10 @@
  *        (dual quantization, error against the original values, min max-error /
  *        MAE / MSE rules), "Implementation details" (tensor scale computed
  *        against an E4M3 limit of 256 instead of 448).
+ *   [P1] section 1 also names MXFP4 as the contrast: 32-element blocks with a
+ *        power-of-two (E8M0) scale.  The pages do not give its scale rule; the
+ *        oracle takes the OCP Microscaling v1.0 one (shared exponent =
+ *        floor(log2 of the block max) minus the largest E2M1 exponent, 2).
  *
  * Arithmetic: IEEE binary32, one rounding (to nearest even) per operation, in
  * the fixed order written in nvfp4_oracle.c.  Built with -ffp-contract=off and
@@ -34,6 +38,10 @@
  *   orc_e2m1_sr -- pinned statistically (unbiasedness) and by its special
  *       cases; the exact random-word-to-decision mapping is a reading, not a
  *       page fact.
+ *   orc_mx_scale_code, orc_mxfp4_* -- pinned by brute force (nearest of the
+ *       scaled grid), the defining range of the scaled block max, the
+ *       row/column transpose identity and the outlier behaviour [P1] section 1
+ *       describes; the scale rule itself is a reading (see above).
  *   op-order choices (block-scale division order, reciprocal-then-multiply,
  *       pairwise error sum) -- parity unpinned by the pages.
  */
@@ -103,6 +111,23 @@ int orc_quantize(const void* x, int dtype, int64_t rows, int64_t cols, const orc
 /* codes [rows][cols/2], scales as above for the given block kind; out [rows][cols] */
 void orc_dequantize(const uint8_t* codes, const uint8_t* scales, float tensor_scale, int64_t rows, int64_t cols,
                     int block_2d, float* out);
+
+/* ---- MXFP4 (the contrast format of [P1] section 1) ----------------------
+ * OCP Microscaling (MX) FP4: 32-element row blocks, each with a power-of-two
+ * scale X = 2^e stored as E8M0 (biased exponent e + 127), no tensor scale.
+ * e = floor(log2(max |y|)) - 2 (2 = the largest exponent of E2M1), clamped to
+ * [-127, 127]; an all-zero block gets e = -127.  Elements: E2M1 rounding of
+ * y / X (nearest-even or stochastic as above), saturating at 6.
+ * Row copy: codes [rows][cols/2] (same packing), scales [rows][cols/32],
+ * cols % 32 == 0.  Column copy (blocks of 32 rows, stored transposed): codes
+ * [cols][rows/2], scales [cols][rows/32], rows % 32 == 0.  Stochastic rounding
+ * uses the element's word from orc_sr_word, as in NVFP4. */
+float orc_e8m0_value(uint8_t code);
+uint8_t orc_mx_scale_code(float block_max);
+int orc_mxfp4_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int emit_row, int emit_col, int sr,
+                       uint64_t sr_seed, int64_t row_offset, uint8_t* codes_row, uint8_t* scales_row,
+                       uint8_t* codes_col, uint8_t* scales_col);
+void orc_mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols, float* out);
 
 /* ---- batch forms of the scalar functions above (same semantics) -------- */
 void orc_e2m1_rne_n(const float* z, int64_t n, uint8_t* out);
