@@ -153,6 +153,50 @@ nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const
  * (stochastic rounding only uses counters whose last word is 0). */
 uint32_t nvfp4_rht_signs_from_seed(uint64_t seed);
 
+/* ---- MXFP4 -----------------------------------------------------------------
+ * The format [P1] section 1 contrasts with NVFP4: 32-element blocks, each with
+ * a power-of-two scale stored as E8M0 (2^(code - 127); code 255 is NaN), and no
+ * tensor scale.  The pages do not give its scale rule; the library follows the
+ * OCP Microscaling v1.0 one: for block max m, the shared exponent is
+ * floor(log2 m) - 2 (2 being the largest E2M1 exponent), clamped to >= -127
+ * (m = 0 and m < 2^-125 give code 0).  Elements: E2M1 of fl(y * 2^-e),
+ * nearest-even or stochastic with the element's Philox word exactly as in
+ * nvfp4_quantize (the same key, counter and decision rule).  Four Over Six
+ * does not apply ([P2]: the power-of-two scale has no room for it). */
+typedef struct {
+  int32_t emit_rowwise;  /* 1x32 row blocks */
+  int32_t emit_colwise;  /* 32x1 column blocks, laid out as the transpose */
+  int32_t sr;            /* 1: stochastic rounding; 0: round to nearest even */
+  uint64_t sr_seed;
+  int64_t row_offset;    /* as in nvfp4_config */
+} nvfp4_mx_config;
+
+/* Device outputs of nvfp4_mxfp4_quantize (a copy not requested may be NULL):
+ *   codes_row  [rows][cols/2]   packed like nvfp4_outputs
+ *   scales_row [rows][cols/32]  E8M0 codes
+ *   codes_col  [cols][rows/2]
+ *   scales_col [cols][rows/32]
+ * codes_* must be 16-byte aligned. */
+typedef struct {
+  uint8_t* codes_row;
+  uint8_t* scales_row;
+  uint8_t* codes_col;
+  uint8_t* scales_col;
+} nvfp4_mx_outputs;
+
+/* One pass over x, no amax needed.  Shapes: cols % 32 == 0; rows % 32 == 0 with a
+ * column copy.  NVFP4_ERR_UNSUPPORTED if no copy is requested.
+ *   x    device, 16-byte aligned;  cfg, out: host pointers */
+nvfp4_status nvfp4_mxfp4_quantize(const void* x, nvfp4_dtype dtype, int64_t rows, int64_t cols,
+                                  const nvfp4_mx_config* cfg, const nvfp4_mx_outputs* out, void* stream);
+
+/* out[r][c] = value(code) * 2^(sc - 127) (exact; NaN where sc == 255).
+ *   codes device [rows][cols/2], 16-byte aligned; scales device [rows][cols/32];
+ *   out device float [rows][cols], 16-byte aligned; cols % 32 == 0.  A column copy
+ *   is dequantized with its own dims (rows = original cols). */
+nvfp4_status nvfp4_mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                                    float* out, void* stream);
+
 const char* nvfp4_status_string(nvfp4_status s);
 int nvfp4_abi_version(void);
 

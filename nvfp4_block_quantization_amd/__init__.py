@@ -47,6 +47,25 @@ class Outputs(ctypes.Structure):
     ]
 
 
+class MXConfig(ctypes.Structure):
+    _fields_ = [
+        ("emit_rowwise", ctypes.c_int32),
+        ("emit_colwise", ctypes.c_int32),
+        ("sr", ctypes.c_int32),
+        ("sr_seed", ctypes.c_uint64),
+        ("row_offset", ctypes.c_int64),
+    ]
+
+
+class MXOutputs(ctypes.Structure):
+    _fields_ = [
+        ("codes_row", ctypes.c_void_p),
+        ("scales_row", ctypes.c_void_p),
+        ("codes_col", ctypes.c_void_p),
+        ("scales_col", ctypes.c_void_p),
+    ]
+
+
 class NVFP4Error(RuntimeError):
     def __init__(self, status: int, what: str):
         super().__init__(f"{what}: {lib().nvfp4_status_string(status).decode()} (status {status})")
@@ -78,6 +97,10 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_quantize.argtypes = [P, i32, i64, i64, ctypes.POINTER(Config), P, ctypes.POINTER(Outputs), P]
         L.nvfp4_dequantize.restype = i32
         L.nvfp4_dequantize.argtypes = [P, P, P, i64, i64, i32, P, P]
+        L.nvfp4_mxfp4_quantize.restype = i32
+        L.nvfp4_mxfp4_quantize.argtypes = [P, i32, i64, i64, ctypes.POINTER(MXConfig), ctypes.POINTER(MXOutputs), P]
+        L.nvfp4_mxfp4_dequantize.restype = i32
+        L.nvfp4_mxfp4_dequantize.argtypes = [P, P, i64, i64, P, P]
         _lib = L
     return _lib
 
@@ -189,4 +212,48 @@ def dequantize(codes: torch.Tensor, scales: torch.Tensor, tensor_scale: torch.Te
     st = lib().nvfp4_dequantize(_ptr(codes), _ptr(scales), _ptr(tensor_scale), rows, cols, BLOCKS[block], _ptr(out),
                                 _stream(codes.device, stream))
     _check(st, "nvfp4_dequantize")
+    return out
+
+
+# ---- MXFP4 (32-element blocks, E8M0 power-of-two scales, no tensor scale) ----
+
+def mxfp4_allocate_outputs(rows: int, cols: int, rowwise: bool = True, colwise: bool = False,
+                           device: torch.device | str = "cuda") -> dict:
+    u8 = dict(dtype=torch.uint8, device=device)
+    o = {}
+    if rowwise:
+        o["codes_row"] = torch.empty((rows, cols // 2), **u8)
+        o["scales_row"] = torch.empty((rows, cols // 32), **u8)
+    if colwise:
+        o["codes_col"] = torch.empty((cols, rows // 2), **u8)
+        o["scales_col"] = torch.empty((cols, rows // 32), **u8)
+    return o
+
+
+def mxfp4_quantize(x: torch.Tensor, rowwise: bool = True, colwise: bool = False, sr: bool = False,
+                   sr_seed: int = 0, row_offset: int = 0, out: dict | None = None,
+                   stream: torch.cuda.Stream | None = None) -> dict:
+    """MXFP4-quantize x (one pass, no amax); returns a dict of output tensors."""
+    _gpu2d(x, "x")
+    rows, cols = x.shape
+    if out is None:
+        out = mxfp4_allocate_outputs(rows, cols, rowwise, colwise, x.device)
+    cfg = MXConfig(int(rowwise), int(colwise), int(sr), sr_seed, row_offset)
+    o = MXOutputs(out["codes_row"].data_ptr() if rowwise else None, out["scales_row"].data_ptr() if rowwise else None,
+                  out["codes_col"].data_ptr() if colwise else None, out["scales_col"].data_ptr() if colwise else None)
+    st = lib().nvfp4_mxfp4_quantize(_ptr(x), _dtype_code(x), rows, cols, ctypes.byref(cfg), ctypes.byref(o),
+                                    _stream(x.device, stream))
+    _check(st, "nvfp4_mxfp4_quantize")
+    return out
+
+
+def mxfp4_dequantize(codes: torch.Tensor, scales: torch.Tensor, rows: int, cols: int,
+                     out: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """fp32 [rows][cols] from packed codes and E8M0 scales."""
+    _gpu2d(codes, "codes")
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float32, device=codes.device)
+    st = lib().nvfp4_mxfp4_dequantize(_ptr(codes), _ptr(scales), rows, cols, _ptr(out),
+                                      _stream(codes.device, stream))
+    _check(st, "nvfp4_mxfp4_dequantize")
     return out

@@ -14,6 +14,9 @@
 //                               LDS and read back by columns; the column copy
 //                               leaves as whole 128-byte lines.
 //   dequant                     codes + scales + S_t -> fp32.
+//   MXFP4                       the row and strip kernels instantiated for
+//                               32-element blocks with E8M0 scales (no tensor
+//                               scale), and mx_dequant.
 #include "nvfp4_device.hpp"
 
 #include <hip/hip_runtime.h>
@@ -220,7 +223,7 @@ __device__ __forceinline__ void unpack_raw(const RawBlock<DT>& r, float* y) {
   }
 }
 
-template <int DT, bool RHT, bool SR, int RULE, int U>
+template <int DT, bool RHT, bool SR, int RULE, int U, bool MX>
 struct RowChunk {
   RawBlock<DT> raw[U];
 
@@ -240,28 +243,39 @@ struct RowChunk {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t b = block(c, u);
-      if (b >= nblocks) continue;
+      if (b >= nblocks) continue;  // MXFP4: nblocks is even, so both lanes of a pair take this branch
       float y[16];
       unpack_raw<DT>(raw[u], y);
       if constexpr (RHT) rht16(y, p.rht_mask);
       uint32_t w[16];
       if constexpr (SR) sr_words16((uint64_t)p.idx_base + (uint64_t)(16 * b), p.k0, p.k1, w);
-      const BlockResult r = quant_block16<SR, RULE>(y, w, tab, ts.den6, ts.den4);
-      reinterpret_cast<uint2*>(p.codes_row)[b] = make_uint2(r.codes.lo, r.codes.hi);
-      p.scales_row[b] = (uint8_t)r.sb;
+      if constexpr (MX) {
+        // a 32-element block is the 16-element halves of lanes 2k and 2k + 1
+        float m = absmax16(y);
+        m = fmaxf(m, dpp<kDppXor1>(m));
+        const uint32_t code = mx_scale_code(m);
+        const BlockCodes cc = mx_round16<SR>(y, code, w);
+        reinterpret_cast<uint2*>(p.codes_row)[b] = make_uint2(cc.lo, cc.hi);
+        if ((b & 1) == 0) p.scales_row[b >> 1] = (uint8_t)code;
+      } else {
+        const BlockResult r = quant_block16<SR, RULE>(y, w, tab, ts.den6, ts.den4);
+        reinterpret_cast<uint2*>(p.codes_row)[b] = make_uint2(r.codes.lo, r.codes.hi);
+        p.scales_row[b] = (uint8_t)r.sb;
+      }
     }
   }
 };
 
-template <int DT, bool RHT, bool SR, int RULE, int U>
+template <int DT, bool RHT, bool SR, int RULE, int U, bool MX>
 __global__ __launch_bounds__(kThreads) void quant_row_kernel(const void* __restrict__ x, int64_t nblocks,
                                                              QuantParams p) {
   __shared__ f32x2 tab[128];
-  const TensorScale ts = workgroup_setup(p, tab);
+  TensorScale ts{};
+  if constexpr (!MX) ts = workgroup_setup(p, tab);
   const int64_t per_chunk = (int64_t)kThreads * U;
   const int64_t nchunks = (nblocks + per_chunk - 1) / per_chunk;
   const int64_t G = gridDim.x;
-  RowChunk<DT, RHT, SR, RULE, U> A, B;
+  RowChunk<DT, RHT, SR, RULE, U, MX> A, B;
   int64_t c = blockIdx.x;
   if (c < nchunks) A.load(x, c, nblocks);
   for (; c < nchunks; c += 2 * G) {
@@ -293,17 +307,29 @@ __device__ __forceinline__ uint32_t xcd_order(uint32_t bid, uint32_t nb) {
   return xcd * q + (xcd < rem ? xcd : rem) + slot;
 }
 
-template <int DT, bool TWO_D, bool SR, int RULE>
+// Block formats of the strip kernel.
+enum StripFormat : int {
+  kFmt1D = 0,  // NVFP4 1x16 row blocks and 16x1 column blocks
+  kFmt2D = 1,  // NVFP4 16x16 tiles, one scale shared by both copies
+  kFmtMX = 2   // MXFP4 1x32 row blocks and 32x1 column blocks
+};
+
+template <int DT, int FMT, bool SR, int RULE>
 __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
                                                                uint32_t strips_x, QuantParams p) {
+  constexpr bool TWO_D = FMT == kFmt2D;
+  constexpr bool MX = FMT == kFmtMX;
   constexpr int VP = 68;  // LDS pitch (dwords) of the staged sub-tile: 64 values + 16 bytes of padding
   constexpr int WP = SR ? 68 : 1;
   constexpr int CP = 36;  // LDS pitch (dwords) of the column-copy codes: 128 bytes + 16 of padding
+  // column-copy scale bytes per column of the strip: 16 (NVFP4 1D), 8 (MXFP4); 2D: 16 per tile column
+  constexpr int SPC = MX ? 8 : 16;
   __shared__ f32x2 tab[128];
   __shared__ float lds_v[64 * VP];
   __shared__ uint32_t lds_w[SR ? 64 * WP : 1];
   __shared__ uint32_t col_codes[64 * CP];
-  __shared__ uint32_t col_scales[TWO_D ? 16 : 256];  // 1D: [64 cols][16 bytes]; 2D: [4 tile cols][16 bytes]
+  __shared__ uint32_t col_scales[TWO_D ? 16 : 64 * SPC / 4];
+  __shared__ float lds_m[MX ? 4 * 64 : 1];  // MXFP4: column maxima of each wave's 16 rows
 
   const uint32_t strip = xcd_order(blockIdx.x, gridDim.x);
   const uint32_t sy = strip / strips_x, sx = strip - sy * strips_x;
@@ -326,7 +352,8 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
   };
   RawBlock<DT> raw, nxt;
   load_sub(0, raw);
-  const TensorScale ts = workgroup_setup(p, tab);
+  TensorScale ts{};
+  if constexpr (!MX) ts = workgroup_setup(p, tab);
 
   for (int q = 0; q < nsub; ++q) {  // uniform trip count
     const int64_t r0 = sr0 + 64 * q + 16 * bi;  // first row of this lane's 16x16 block
@@ -339,12 +366,23 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
     unpack_raw<DT>(raw, y);
     if constexpr (SR) sr_words16((uint64_t)((p.row_offset + r0 + i) * cols + c0), p.k0, p.k1, w);
     BlockResult res;
-    if constexpr (TWO_D) res = quant_tile_row16<SR, RULE>(y, w, tab, ts.den6, ts.den4);
-    else res = quant_block16<SR, RULE>(y, w, tab, ts.den6, ts.den4);
+    if constexpr (MX) {
+      // the 32-column block of columns c0 .. is shared with lane t ^ 16 (bj ^ 1)
+      float m = absmax16(y);
+      m = fmaxf(m, swizzle_xor16(m));
+      res.sb = mx_scale_code(m);
+      res.codes = mx_round16<SR>(y, res.sb, w);
+    } else if constexpr (TWO_D) {
+      res = quant_tile_row16<SR, RULE>(y, w, tab, ts.den6, ts.den4);
+    } else {
+      res = quant_block16<SR, RULE>(y, w, tab, ts.den6, ts.den4);
+    }
 
     if (valid && p.emit_row) {
       *reinterpret_cast<uint2*>(p.codes_row + (r0 + i) * (cols / 2) + c0 / 2) = make_uint2(res.codes.lo, res.codes.hi);
-      if constexpr (TWO_D) {
+      if constexpr (MX) {
+        if ((bj & 1) == 0) p.scales_row[(r0 + i) * (cols / 32) + c0 / 32] = (uint8_t)res.sb;
+      } else if constexpr (TWO_D) {
         if (i == 0) p.scales_row[(r0 / 16) * (cols / 16) + c0 / 16] = (uint8_t)res.sb;
       } else {
         p.scales_row[(r0 + i) * (cols / 16) + c0 / 16] = (uint8_t)res.sb;
@@ -377,10 +415,19 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
       y[k] = lds_v[row * VP + col];
       if constexpr (SR) w[k] = lds_w[row * WP + col];
     }
+    float mcol = 0.0f;
+    if constexpr (MX) {
+      // a 32-row block spans waves 2h and 2h + 1: swap the column maxima through LDS
+      mcol = absmax16(y);
+      lds_m[bi * 64 + col] = mcol;
+    }
     __syncthreads();  // the next sub-tile overwrites the staging area
     BlockCodes cc;
     uint32_t sbc;
-    if constexpr (TWO_D) {
+    if constexpr (MX) {
+      sbc = mx_scale_code(fmaxf(mcol, lds_m[(bi ^ 1) * 64 + col]));
+      cc = mx_round16<SR>(y, sbc, w);
+    } else if constexpr (TWO_D) {
       // same values, same reciprocal, same words: the codes of the row copy, transposed
       if constexpr (SR) {
 #pragma unroll
@@ -393,12 +440,15 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
       cc = rc.codes;
       sbc = rc.sb;
     }
-    // collect: column `col`, bytes 32q + 8bi .. of its 128-byte line; scale byte 4q + bi
+    // collect: column `col`, bytes 32q + 8bi .. of its 128-byte line; scale byte 4q + bi (MXFP4: 2q + bi/2)
     *reinterpret_cast<uint2*>(col_codes + col * CP + 8 * q + 2 * bi) = make_uint2(cc.lo, cc.hi);
-    if constexpr (TWO_D) {
-      if (i == 0) reinterpret_cast<uint8_t*>(col_scales)[bj * 16 + 4 * q + bi] = (uint8_t)sbc;
+    uint8_t* csb = reinterpret_cast<uint8_t*>(col_scales);
+    if constexpr (MX) {
+      if ((bi & 1) == 0) csb[col * SPC + 2 * q + (bi >> 1)] = (uint8_t)sbc;
+    } else if constexpr (TWO_D) {
+      if (i == 0) csb[bj * 16 + 4 * q + bi] = (uint8_t)sbc;
     } else {
-      reinterpret_cast<uint8_t*>(col_scales)[col * 16 + 4 * q + bi] = (uint8_t)sbc;
+      csb[col * SPC + 4 * q + bi] = (uint8_t)sbc;
     }
     raw = nxt;
   }
@@ -406,7 +456,7 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
   __syncthreads();
 
   // ---- write the strip's column copy: per column, rows_valid / 2 code bytes
-  // and rows_valid / 16 scale bytes, contiguous in the output
+  // and rows_valid / 16 (MXFP4: / 32) scale bytes, contiguous in the output
   const int rows_valid = (int)(rows_left < kStripRows ? rows_left : kStripRows);  // a multiple of 16
   const int cbytes = rows_valid / 2;
   const bool wide = ((rows / 2) & 15) == 0;  // every column's line starts 16-byte aligned
@@ -425,21 +475,23 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
       if (16 * part + 16 <= cbytes) *reinterpret_cast<uint2*>(dst + 8) = make_uint2(v.z, v.w);
     }
   }
-  const int sbytes = rows_valid / 16;  // scale bytes per column (1D) or per tile column (2D)
   const uint8_t* cs = reinterpret_cast<const uint8_t*>(col_scales);
   if constexpr (TWO_D) {
+    const int sbytes = rows_valid / 16;  // scale bytes per tile column
     if (t < 4 * 16) {
       const int tc = t >> 4, j = t & 15;
       const int64_t ctile = (int64_t)sx * 4 + tc;
       if (ctile * 16 < cols && j < sbytes) p.scales_col[ctile * (rows / 16) + sr0 / 16 + j] = cs[tc * 16 + j];
     }
   } else {
+    constexpr int BR = MX ? 32 : 16;  // rows per column block
+    const int sbytes = rows_valid / BR;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = t + kThreads * j;  // 64 columns x 16 bytes
-      const int colk = k >> 4, b = k & 15;
+    for (int j = 0; j < 64 * SPC / kThreads; ++j) {
+      const int k = t + kThreads * j;  // 64 columns x SPC bytes
+      const int colk = k / SPC, b = k % SPC;
       const int64_t c = (int64_t)sx * 64 + colk;
-      if (c < cols && b < sbytes) p.scales_col[c * (rows / 16) + sr0 / 16 + b] = cs[colk * 16 + b];
+      if (c < cols && b < sbytes) p.scales_col[c * (rows / BR) + sr0 / BR + b] = cs[colk * SPC + b];
     }
   }
 }
@@ -468,6 +520,32 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
       sb = scales[b];
     }
     const float d = e4m3_decode(sb) * st;
+    f32x2 v[8];
+    v[0] = fp4_pair_values<0>(c.x);
+    v[1] = fp4_pair_values<1>(c.x);
+    v[2] = fp4_pair_values<2>(c.x);
+    v[3] = fp4_pair_values<3>(c.x);
+    v[4] = fp4_pair_values<0>(c.y);
+    v[5] = fp4_pair_values<1>(c.y);
+    v[6] = fp4_pair_values<2>(c.y);
+    v[7] = fp4_pair_values<3>(c.y);
+    float4* o = reinterpret_cast<float4*>(out + 16 * b);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = make_float4(v[2 * j].x * d, v[2 * j].y * d, v[2 * j + 1].x * d, v[2 * j + 1].y * d);
+  }
+}
+
+// MXFP4: out = value(code) * 2^(sc - 127); E8M0 code 255 is NaN.
+__global__ __launch_bounds__(kThreads) void mx_dequant_kernel(const uint8_t* __restrict__ codes,
+                                                              const uint8_t* __restrict__ scales, int64_t nblocks,
+                                                              float* __restrict__ out) {
+  const int64_t nth = (int64_t)gridDim.x * kThreads;
+  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += nth) {
+    const uint2 c = *reinterpret_cast<const uint2*>(codes + 8 * b);
+    const uint32_t sc = scales[b >> 1];  // 16 elements: half of a 32-element block
+    const float d = sc == 0u ? __uint_as_float(0x00400000u)
+                             : (sc == 255u ? __uint_as_float(0x7FC00000u) : __uint_as_float(sc << 23));
     f32x2 v[8];
     v[0] = fp4_pair_values<0>(c.x);
     v[1] = fp4_pair_values<1>(c.x);
@@ -660,7 +738,7 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dtype, int64_t rows, int6
       with_bool(cfg->rht != 0, [&](auto RHT) {
         with_bool(cfg->sr != 0, [&](auto SR) {
           with_rule(cfg->rule, [&](auto RULE) {
-            auto k = quant_row_kernel<DT(), RHT(), SR(), RULE(), kRowU>;
+            auto k = quant_row_kernel<DT(), RHT(), SR(), RULE(), kRowU, false>;
             int64_t grid = resident_grid(k);
             if (grid > nchunks) grid = nchunks;
             hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), 0, s, x, nblocks, p);
@@ -676,7 +754,8 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dtype, int64_t rows, int6
       with_bool(two_d, [&](auto TWO_D) {
         with_bool(cfg->sr != 0, [&](auto SR) {
           with_rule(cfg->rule, [&](auto RULE) {
-            hipLaunchKernelGGL((quant_strip_kernel<DT(), TWO_D(), SR(), RULE()>), dim3((unsigned)nstrips),
+            constexpr int FMT = TWO_D() ? kFmt2D : kFmt1D;
+            hipLaunchKernelGGL((quant_strip_kernel<DT(), FMT, SR(), RULE()>), dim3((unsigned)nstrips),
                                dim3(kThreads), 0, s, x, rows, cols, (uint32_t)strips_x, p);
           });
         });
@@ -703,6 +782,76 @@ nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const
     hipLaunchKernelGGL((dequant_kernel<TWO_D()>), dim3((unsigned)grid), dim3(kThreads), 0, s, codes, scales,
                        tensor_scale, nblocks, cols, out);
   });
+  return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+nvfp4_status nvfp4_mxfp4_quantize(const void* x, nvfp4_dtype dtype, int64_t rows, int64_t cols,
+                                  const nvfp4_mx_config* cfg, const nvfp4_mx_outputs* out, void* stream) {
+  if (!cfg || !out) return NVFP4_ERR_NULL;
+  if (dtype != NVFP4_IN_BF16 && dtype != NVFP4_IN_F32) return NVFP4_ERR_DTYPE;
+  const bool erow = cfg->emit_rowwise != 0, ecol = cfg->emit_colwise != 0;
+  if (!erow && !ecol) return NVFP4_ERR_UNSUPPORTED;
+  if (rows < 0 || cols < 0 || cols % 32) return NVFP4_ERR_SHAPE;
+  if (ecol && rows % 32) return NVFP4_ERR_SHAPE;
+  const int64_t n = rows * cols;
+  if (n == 0) return NVFP4_OK;
+  if (!x) return NVFP4_ERR_NULL;
+  if (erow && (!out->codes_row || !out->scales_row)) return NVFP4_ERR_NULL;
+  if (ecol && (!out->codes_col || !out->scales_col)) return NVFP4_ERR_NULL;
+  if (!aligned16(x)) return NVFP4_ERR_ALIGN;
+  if (erow && !aligned16(out->codes_row)) return NVFP4_ERR_ALIGN;
+  if (ecol && !aligned16(out->codes_col)) return NVFP4_ERR_ALIGN;
+
+  QuantParams p{};
+  p.k0 = (uint32_t)cfg->sr_seed;
+  p.k1 = (uint32_t)(cfg->sr_seed >> 32);
+  p.row_offset = cfg->row_offset;
+  p.idx_base = cfg->row_offset * cols;
+  p.emit_row = erow;
+  p.emit_col = ecol;
+  p.codes_row = out->codes_row;
+  p.scales_row = out->scales_row;
+  p.codes_col = out->codes_col;
+  p.scales_col = out->scales_col;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (!ecol) {
+    const int64_t nblocks = n / 16;
+    const int64_t per_wg = (int64_t)kThreads * kRowU;
+    const int64_t nchunks = (nblocks + per_wg - 1) / per_wg;
+    with_dtype(dtype, [&](auto DT) {
+      with_bool(cfg->sr != 0, [&](auto SR) {
+        auto k = quant_row_kernel<DT(), false, SR(), kRuleNone, kRowU, true>;
+        int64_t grid = resident_grid(k);
+        if (grid > nchunks) grid = nchunks;
+        hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), 0, s, x, nblocks, p);
+      });
+    });
+  } else {
+    const int64_t strips_x = (cols + 63) / 64, strips_y = (rows + kStripRows - 1) / kStripRows;
+    const int64_t nstrips = strips_x * strips_y;
+    if (nstrips > (1ll << 24)) return NVFP4_ERR_SHAPE;
+    with_dtype(dtype, [&](auto DT) {
+      with_bool(cfg->sr != 0, [&](auto SR) {
+        hipLaunchKernelGGL((quant_strip_kernel<DT(), kFmtMX, SR(), kRuleNone>), dim3((unsigned)nstrips),
+                           dim3(kThreads), 0, s, x, rows, cols, (uint32_t)strips_x, p);
+      });
+    });
+  }
+  return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+nvfp4_status nvfp4_mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                                    float* out, void* stream) {
+  if (rows < 0 || cols < 0 || cols % 32) return NVFP4_ERR_SHAPE;
+  const int64_t n = rows * cols;
+  if (n == 0) return NVFP4_OK;
+  if (!codes || !scales || !out) return NVFP4_ERR_NULL;
+  if (!aligned16(codes) || !aligned16(out)) return NVFP4_ERR_ALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t nblocks = n / 16;
+  int64_t grid = (nblocks + kThreads - 1) / kThreads;
+  if (grid > 65536) grid = 65536;
+  hipLaunchKernelGGL(mx_dequant_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, codes, scales, nblocks, out);
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 

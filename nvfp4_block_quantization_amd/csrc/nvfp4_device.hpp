@@ -437,4 +437,45 @@ __device__ __forceinline__ BlockResult quant_tile_row16(const float* y, const ui
   }
 }
 
+// ----------------------------------------------------------------- MXFP4 ---
+
+// MXFP4 (the 32-element, power-of-two-scale format that "Pretraining Large
+// Language Models with NVFP4" section 1 contrasts with NVFP4), with the OCP
+// Microscaling scale rule: the shared exponent is floor(log2 m) - 2 for the
+// block max m (2 = the largest E2M1 exponent), stored as E8M0 with bias 127
+// and floored at code 0 (2^-127, also for m = 0 and subnormal m).  For a
+// normal m, floor(log2 m) + 127 is its biased exponent field.
+__device__ __forceinline__ uint32_t mx_scale_code(float m) {
+  const uint32_t be = __float_as_uint(m) >> 23;  // m >= 0
+  return be > 2u ? be - 2u : 0u;
+}
+
+// 2^(127 - code), the factor that scales the block into the E2M1 range.  For
+// finite inputs code <= 252, so the factor is a normal binary32 and y * factor
+// is the exact quotient y / 2^e rounded once.
+__device__ __forceinline__ float mx_inv_scale(uint32_t code) { return __uint_as_float((254u - code) << 23); }
+
+__device__ __forceinline__ float absmax16(const float* y) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(y[i]));
+  return m;
+}
+
+// Lane l reads lane l ^ 16 (ds_swizzle bitmask mode: and 0x1F, or 0, xor 0x10).
+__device__ __forceinline__ float swizzle_xor16(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+}
+
+// Codes of 16 elements of a 32-element block whose scale code is `code`.
+template <bool SR>
+__device__ __forceinline__ BlockCodes mx_round16(const float* y, uint32_t code, const uint32_t* w) {
+  uint32_t ws[16];
+  if constexpr (SR) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) ws[k] = (k & 1) ? (w[k] >> 1) : w[k];
+  }
+  return round16<SR>(y, mx_inv_scale(code), ws);
+}
+
 }  // namespace nvfp4

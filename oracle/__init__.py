@@ -51,7 +51,8 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        src_mtime = max(os.path.getmtime(_SRC), os.path.getmtime(os.path.join(_HERE, "nvfp4_oracle.h")))
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < src_mtime:
             build()
         L = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p

@@ -487,7 +487,8 @@ void orc_dequantize(const uint8_t* codes, const uint8_t* scales, float tensor_sc
 /* MXFP4: 32-element blocks with power-of-two (E8M0) scales                   */
 /* ------------------------------------------------------------------------ */
 
-float orc_e8m0_value(uint8_t code) { return (float)ldexp(1.0, (int)code - 127); }
+/* E8M0: 2^(code - 127); the code 255 is NaN in the MX specification. */
+float orc_e8m0_value(uint8_t code) { return code == 255 ? NAN : (float)ldexp(1.0, (int)code - 127); }
 
 /* Shared exponent of a block: floor(log2(m)) - 2, so that the block max
  * scales into [4, 8); clamped to the E8M0 range [-127, 127]. */
@@ -562,7 +563,7 @@ void orc_mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t r
       uint8_t byte = codes[r * (cols / 2) + c / 2];
       uint8_t code = (c & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
       uint8_t sc = scales[r * (cols / 32) + c / 32];
-      out[r * cols + c] = (float)ldexp((double)orc_e2m1_value(code), (int)sc - 127);
+      out[r * cols + c] = (float)((double)orc_e2m1_value(code) * (double)orc_e8m0_value(sc));
     }
   }
 }

@@ -87,3 +87,29 @@ def test_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     with pytest.raises(TypeError):
         nv.amax(torch.zeros(16, 16, dtype=torch.bfloat16))
+
+
+def _mx(rows=64, cols=64, x=FAKE, dtype=0, cfg=None, outs=None):
+    cfg = cfg or nv.MXConfig(1, 0, 0, 0, 0)
+    outs = outs or nv.MXOutputs(FAKE, FAKE, FAKE, FAKE)
+    return nv.lib().nvfp4_mxfp4_quantize(ctypes.c_void_p(x) if x else None, dtype, rows, cols, ctypes.byref(cfg),
+                                         ctypes.byref(outs), None)
+
+
+def test_mxfp4_validation():
+    assert _mx(cols=48) == nv.ERR_SHAPE
+    assert _mx(rows=-32) == nv.ERR_SHAPE
+    assert _mx(rows=48, cfg=nv.MXConfig(0, 1, 0, 0, 0)) == nv.ERR_SHAPE
+    assert _mx(cfg=nv.MXConfig(0, 0, 0, 0, 0)) == nv.ERR_UNSUPPORTED
+    assert _mx(dtype=2) == nv.ERR_DTYPE
+    assert _mx(x=0) == nv.ERR_NULL
+    assert _mx(outs=nv.MXOutputs(FAKE, None, None, None)) == nv.ERR_NULL
+    assert _mx(cfg=nv.MXConfig(1, 1, 0, 0, 0), outs=nv.MXOutputs(FAKE, FAKE, FAKE, None)) == nv.ERR_NULL
+    assert _mx(x=FAKE + 8) == nv.ERR_ALIGN
+    assert _mx(outs=nv.MXOutputs(FAKE + 4, FAKE, None, None)) == nv.ERR_ALIGN
+    assert _mx(rows=0) == nv.OK  # empty: nothing to do
+    P = ctypes.c_void_p
+    L = nv.lib()
+    assert L.nvfp4_mxfp4_dequantize(P(FAKE), P(FAKE), 32, 48, P(FAKE), None) == nv.ERR_SHAPE
+    assert L.nvfp4_mxfp4_dequantize(None, P(FAKE), 32, 32, P(FAKE), None) == nv.ERR_NULL
+    assert L.nvfp4_mxfp4_dequantize(P(FAKE), P(FAKE), 32, 32, P(FAKE + 4), None) == nv.ERR_ALIGN
