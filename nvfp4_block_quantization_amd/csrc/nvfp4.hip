@@ -341,30 +341,35 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
   const int nsub = (int)((rows_left < kStripRows ? rows_left : kStripRows) + 63) / 64;
   const bool col_ok = c0 < cols;
 
+  // Element index of this lane's first element in sub-tile q: e(q) = e(0) + q * 64 * cols.
+  // Input, output and random-stream addresses all advance by that uniform stride.
+  const int64_t e_step = 64 * cols;
+  auto lane_valid = [&](int q) { return col_ok && sr0 + 64 * q + 16 * bi < rows; };  // whole 16x16 blocks
   // Input of sub-tile q for this lane (lanes of blocks outside the tensor read
   // its first elements and store nothing).
-  auto load_sub = [&](int q, RawBlock<DT>& raw) {
-    const int64_t r0 = sr0 + 64 * q + 16 * bi;
-    const int64_t e0 = (col_ok && r0 < rows) ? (r0 + i) * cols + c0 : 0;
-    const uint4* src = reinterpret_cast<const uint4*>(x) + e0 / (DT == kBF16 ? 8 : 4);
+  auto load_sub = [&](int q, int64_t e, RawBlock<DT>& raw) {
+    const int64_t e0 = lane_valid(q) ? e : 0;
+    const uint4* src = reinterpret_cast<const uint4*>(x) + (e0 >> (DT == kBF16 ? 3 : 2));
 #pragma unroll
     for (int j = 0; j < (DT == kBF16 ? 2 : 4); ++j) raw.v[j] = src[j];
   };
-  RawBlock<DT> raw, nxt;
-  load_sub(0, raw);
+  const int64_t e_first = (sr0 + 16 * bi + i) * cols + c0;
+  RawBlock<DT> buf0, buf1;
+  load_sub(0, e_first, buf0);
   TensorScale ts{};
   if constexpr (!MX) ts = workgroup_setup(p, tab);
 
-  for (int q = 0; q < nsub; ++q) {  // uniform trip count
+  // One 64x64 sub-tile; prefetches sub-tile q + 1 into `nxt`.
+  auto sub_tile = [&](int q, int64_t e, const RawBlock<DT>& raw, RawBlock<DT>& nxt) {
     const int64_t r0 = sr0 + 64 * q + 16 * bi;  // first row of this lane's 16x16 block
-    const bool valid = col_ok && r0 < rows;     // whole 16x16 blocks: rows, cols are multiples of 16
-    if (q + 1 < nsub) load_sub(q + 1, nxt);    // prefetch the next sub-tile
+    const bool valid = lane_valid(q);
+    if (q + 1 < nsub) load_sub(q + 1, e + e_step, nxt);
 
-    // ---- row pass: lane i holds row r0 + i, columns c0 .. c0 + 15
+    // ---- row pass: lane i holds row r0 + i, columns c0 .. c0 + 15 (element index e ..)
     float y[16];
     uint32_t w[16];
     unpack_raw<DT>(raw, y);
-    if constexpr (SR) sr_words16((uint64_t)((p.row_offset + r0 + i) * cols + c0), p.k0, p.k1, w);
+    if constexpr (SR) sr_words16((uint64_t)(e + p.idx_base), p.k0, p.k1, w);
     BlockResult res;
     if constexpr (MX) {
       // the 32-column block of columns c0 .. is shared with lane t ^ 16 (bj ^ 1)
@@ -379,19 +384,16 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
     }
 
     if (valid && p.emit_row) {
-      *reinterpret_cast<uint2*>(p.codes_row + (r0 + i) * (cols / 2) + c0 / 2) = make_uint2(res.codes.lo, res.codes.hi);
+      *reinterpret_cast<uint2*>(p.codes_row + (e >> 1)) = make_uint2(res.codes.lo, res.codes.hi);
       if constexpr (MX) {
-        if ((bj & 1) == 0) p.scales_row[(r0 + i) * (cols / 32) + c0 / 32] = (uint8_t)res.sb;
+        if ((bj & 1) == 0) p.scales_row[e >> 5] = (uint8_t)res.sb;
       } else if constexpr (TWO_D) {
         if (i == 0) p.scales_row[(r0 / 16) * (cols / 16) + c0 / 16] = (uint8_t)res.sb;
       } else {
-        p.scales_row[(r0 + i) * (cols / 16) + c0 / 16] = (uint8_t)res.sb;
+        p.scales_row[e >> 4] = (uint8_t)res.sb;
       }
     }
-    if (!p.emit_col) {  // uniform across the workgroup
-      raw = nxt;
-      continue;
-    }
+    if (!p.emit_col) return;  // uniform across the workgroup
 
     // ---- stage the sub-tile (and its random words) in LDS as binary32
     {
@@ -450,7 +452,14 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
     } else {
       csb[col * SPC + 4 * q + bi] = (uint8_t)sbc;
     }
-    raw = nxt;
+  };
+
+  // Two sub-tiles per trip so that the prefetch buffers alternate without copies.
+  int64_t e = e_first;
+  for (int q = 0; q < nsub; q += 2) {  // uniform trip count
+    sub_tile(q, e, buf0, buf1);
+    if (q + 1 < nsub) sub_tile(q + 1, e + e_step, buf1, buf0);
+    e += 2 * e_step;
   }
   if (!p.emit_col) return;
   __syncthreads();
