@@ -82,6 +82,7 @@ def lib():
             "orc_mx_scale_code": (ctypes.c_uint8, [f32]),
             "orc_mxfp4_quantize": (i32, [P, i32, i64, i64, i32, i32, i32, u64, i64, P, P, P, P]),
             "orc_mxfp4_dequantize": (None, [P, P, i64, i64, P]),
+            "orc_error_stats": (i32, [P, i32, i64, i64, ctypes.POINTER(Config), f32, f32, i32, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -277,4 +278,18 @@ def mxfp4_dequantize(codes: np.ndarray, scales: np.ndarray, rows: int, cols: int
     scales = np.ascontiguousarray(scales, dtype=np.uint8)
     out = np.empty((rows, cols), np.float32)
     lib().orc_mxfp4_dequantize(_ptr(codes), _ptr(scales), rows, cols, _ptr(out))
+    return out
+
+
+# ---- error analysis ------------------------------------------------------------
+
+def error_stats(x: np.ndarray, cfg: Config, a: float, bin_width: float = 0.25, nbins: int = 26) -> np.ndarray:
+    """(3, nbins) float64: per scaled-value bin, the element count, the sum of
+    squared errors of the quantized path and of the exact-scale reference."""
+    x = np.ascontiguousarray(x)
+    M, N = x.shape
+    out = np.zeros((3, nbins), np.float64)
+    rc = lib().orc_error_stats(_ptr(x), _dtype_code(x), M, N, ctypes.byref(cfg), a, bin_width, nbins, _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the error-analysis arguments (code {rc})")
     return out

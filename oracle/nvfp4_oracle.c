@@ -484,6 +484,96 @@ void orc_dequantize(const uint8_t* codes, const uint8_t* scales, float tensor_sc
 }
 
 /* ------------------------------------------------------------------------ */
+/* Error analysis by scaled value ([P2] "Problem statement")                  */
+/* ------------------------------------------------------------------------ */
+
+/* Nearest E2M1 magnitude to q >= 0 (binary64), ties to the even grid index. */
+static double e2m1_nearest64(double q) {
+  if (q >= 6.0) return 6.0;
+  int best = 0;
+  double bestd = fabs(q - kE2M1[0]);
+  for (int k = 1; k < 8; ++k) {
+    double d = fabs(q - kE2M1[k]);
+    if (d < bestd || (d == bestd && (k % 2) == 0)) {
+      best = k;
+      bestd = d;
+    }
+  }
+  return kE2M1[best];
+}
+
+/* Per block: the quantized path exactly as orc_quantize computes it (RNE), and
+ * a reference with an unquantized scale: the block max maps exactly to T (the
+ * candidate the block chose), v* = nearest-even E2M1 of q = fl64(T*|y| / m_b),
+ * xh* = fl64(v* * m_b / T) with the sign of y.  Each element lands in the bin of
+ * its scaled value |z|, z = fl(y * e); per bin the element count, the sum of
+ * eps^2 (eps = fl(y - fl(v * d))) and the sum of eps*^2 (eps* = fl64(y - xh*))
+ * are accumulated in binary64 in element order. */
+static void err_block(const float* y, int n, float s_t, int rule, float inv_w, int nbins, double* stats) {
+  uint8_t codes[256], sb, ch;
+  float err[2];
+  orc_quantize_block(y, n, s_t, rule, 0, NULL, codes, &sb, &ch, err);
+  const double T = ch ? 4.0 : 6.0;
+  float d = orc_e4m3_value(sb) * s_t;
+  float e = 0.0f;
+  if (d != 0.0f) {
+    e = 1.0f / d;
+    if (isinf(e)) e = 0.0f;
+  }
+  float m_b = 0.0f;
+  for (int i = 0; i < n; ++i)
+    if (fabsf(y[i]) > m_b) m_b = fabsf(y[i]);
+  for (int i = 0; i < n; ++i) {
+    float z = y[i] * e;
+    int b = (int)floorf(fabsf(z) * inv_w); /* exact: inv_w is a power of two */
+    if (b > nbins - 1) b = nbins - 1;
+    float xh = orc_e2m1_value(codes[i]) * d;
+    float eps = y[i] - xh;
+    double xs = 0.0;
+    if (m_b != 0.0f) {
+      double q = (T * fabs((double)y[i])) / (double)m_b;
+      xs = (e2m1_nearest64(q) * (double)m_b) / T;
+    }
+    double eps_s = (double)y[i] - copysign(xs, (double)y[i]);
+    stats[b] += 1.0;
+    stats[nbins + b] += (double)eps * (double)eps;
+    stats[2 * nbins + b] += eps_s * eps_s;
+  }
+}
+
+int orc_error_stats(const void* x, int dtype, int64_t rows, int64_t cols, const orc_config* cfg, float amax,
+                    float bin_width, int nbins, double* stats) {
+  if (rows < 0 || cols < 0 || cols % 16 || rows % 16 || nbins < 1 || nbins > 64) return 1;
+  if (cfg->sr || (cfg->rht && cfg->block_2d)) return 1;
+  int eb;
+  if (!(bin_width > 0.0f) || frexpf(bin_width, &eb) != 0.5f) return 1; /* a power of two */
+  const float inv_w = 1.0f / bin_width;
+  const float s_t = orc_tensor_scale(amax, cfg->cap);
+  memset(stats, 0, sizeof(double) * 3 * (size_t)nbins);
+  float y[256];
+  if (cfg->block_2d) {
+    for (int64_t tr = 0; tr < rows / 16; ++tr)
+      for (int64_t tc = 0; tc < cols / 16; ++tc) {
+        for (int i = 0; i < 16; ++i)
+          for (int j = 0; j < 16; ++j) y[i * 16 + j] = load_elem(x, dtype, (tr * 16 + i) * cols + tc * 16 + j);
+        err_block(y, 256, s_t, cfg->rule, inv_w, nbins, stats);
+      }
+    return 0;
+  }
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t j = 0; j < cols / 16; ++j) {
+      for (int k = 0; k < 16; ++k) y[k] = load_elem(x, dtype, r * cols + j * 16 + k);
+      if (cfg->rht) {
+        float t[16];
+        orc_rht16(y, cfg->rht_mask, t);
+        memcpy(y, t, sizeof(t));
+      }
+      err_block(y, 16, s_t, cfg->rule, inv_w, nbins, stats);
+    }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* MXFP4: 32-element blocks with power-of-two (E8M0) scales                   */
 /* ------------------------------------------------------------------------ */
 

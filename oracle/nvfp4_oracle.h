@@ -38,6 +38,10 @@
  *   orc_e2m1_sr -- pinned statistically (unbiasedness) and by its special
  *       cases; the exact random-word-to-decision mapping is a reading, not a
  *       page fact.
+ *   orc_error_stats -- pinned by the total squared error of orc_quantize +
+ *       orc_dequantize, brute-force exact-scale rounding with rationals, and
+ *       the concentration of error near the scaled value 5 that [P2]
+ *       "Problem statement" reports.
  *   orc_mx_scale_code, orc_mxfp4_* -- pinned by brute force (nearest of the
  *       scaled grid), the defining range of the scaled block max, the
  *       row/column transpose identity and the outlier behaviour [P1] section 1
@@ -111,6 +115,19 @@ int orc_quantize(const void* x, int dtype, int64_t rows, int64_t cols, const orc
 /* codes [rows][cols/2], scales as above for the given block kind; out [rows][cols] */
 void orc_dequantize(const uint8_t* codes, const uint8_t* scales, float tensor_scale, int64_t rows, int64_t cols,
                     int block_2d, float* out);
+
+/* ---- error analysis ([P2] "Problem statement": the error of values near the
+ * block max, around the scaled value 5, dominates; the scale factor's own
+ * quantization matters little) ------------------------------------------------
+ * Round-to-nearest NVFP4 as orc_quantize computes it (1x16 row blocks, with the
+ * transform if cfg->rht, or 16x16 tiles; cfg->rule chooses 4/6), plus a
+ * reference with an exact scale (the block max maps exactly to the chosen T).
+ * Elements are binned by their scaled value |z| in bins of width bin_width (a
+ * power of two; the last bin takes everything above).  stats[3][nbins]
+ * (binary64): element count, sum of eps^2, sum of eps*^2 (exact-scale error).
+ * rows % 16 == 0, cols % 16 == 0, 1 <= nbins <= 64, no stochastic rounding. */
+int orc_error_stats(const void* x, int dtype, int64_t rows, int64_t cols, const orc_config* cfg, float amax,
+                    float bin_width, int nbins, double* stats);
 
 /* ---- MXFP4 (the contrast format of [P1] section 1) ----------------------
  * OCP Microscaling (MX) FP4: 32-element row blocks, each with a power-of-two
