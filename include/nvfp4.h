@@ -153,6 +153,31 @@ nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const
  * (stochastic rounding only uses counters whose last word is 0). */
 uint32_t nvfp4_rht_signs_from_seed(uint64_t seed);
 
+/* ---- error analysis ----------------------------------------------------------
+ * [P2] "Problem statement": the error of values near the block max (around the
+ * scaled value 5) dominates, and the quantization of the scale factor itself
+ * matters little.  This call measures both on a tensor.  It quantizes x with
+ * round-to-nearest exactly as nvfp4_quantize does (cfg->block, rht, rule and
+ * scale_cap; 1x16 row blocks or 16x16 tiles; sr must be 0 and the emit flags
+ * are ignored) and bins every element by its scaled value |z|, z = fl(y * e), in
+ * bins [k * bin_width, (k + 1) * bin_width) (the last bin takes everything
+ * above).  stats_dev receives three rows of nbins doubles:
+ *   [0][k]  number of elements in bin k (exact)
+ *   [1][k]  sum of eps^2, eps = fl(y - fl(v * d)) (the dequantized error)
+ *   [2][k]  sum of eps*^2 for a reference with an unquantized scale: the block max
+ *           maps exactly onto the chosen T, v* = nearest-even E2M1 of T|y| / m_b,
+ *           eps* = fl64(y - fl64(v* * m_b / T)) with the sign of y
+ * Sums are accumulated in binary64 in an unspecified order: each sum of n terms
+ * is within a relative n * 2^-53 of the exact one.  The call overwrites all
+ * 3 * nbins values.  rows % 16 == 0, cols % 16 == 0; bin_width a power of two;
+ * 1 <= nbins <= 64 (NVFP4_ERR_UNSUPPORTED otherwise, also for sr or rht with 2D).
+ *   x          device, 16-byte aligned;  cfg: host pointer
+ *   amax_dev   device, one float (the tensor amax, e.g. from nvfp4_amax)
+ *   stats_dev  device, 3 * nbins doubles */
+nvfp4_status nvfp4_error_stats(const void* x, nvfp4_dtype dtype, int64_t rows, int64_t cols, const nvfp4_config* cfg,
+                               const float* amax_dev, float bin_width, int32_t nbins, double* stats_dev,
+                               void* stream);
+
 /* ---- MXFP4 -----------------------------------------------------------------
  * The format [P1] section 1 contrasts with NVFP4: 32-element blocks, each with
  * a power-of-two scale stored as E8M0 (2^(code - 127); code 255 is NaN), and no

@@ -97,6 +97,9 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_quantize.argtypes = [P, i32, i64, i64, ctypes.POINTER(Config), P, ctypes.POINTER(Outputs), P]
         L.nvfp4_dequantize.restype = i32
         L.nvfp4_dequantize.argtypes = [P, P, P, i64, i64, i32, P, P]
+        L.nvfp4_error_stats.restype = i32
+        L.nvfp4_error_stats.argtypes = [P, i32, i64, i64, ctypes.POINTER(Config), P, ctypes.c_float, ctypes.c_int32,
+                                        P, P]
         L.nvfp4_mxfp4_quantize.restype = i32
         L.nvfp4_mxfp4_quantize.argtypes = [P, i32, i64, i64, ctypes.POINTER(MXConfig), ctypes.POINTER(MXOutputs), P]
         L.nvfp4_mxfp4_dequantize.restype = i32
@@ -212,6 +215,22 @@ def dequantize(codes: torch.Tensor, scales: torch.Tensor, tensor_scale: torch.Te
     st = lib().nvfp4_dequantize(_ptr(codes), _ptr(scales), _ptr(tensor_scale), rows, cols, BLOCKS[block], _ptr(out),
                                 _stream(codes.device, stream))
     _check(st, "nvfp4_dequantize")
+    return out
+
+
+def error_stats(x: torch.Tensor, amax_t: torch.Tensor, block: str = "1d", rht: bool = False, rht_mask: int = 0,
+                rule: str = "none", scale_cap: float = 448.0, bin_width: float = 0.25, nbins: int = 26,
+                out: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """(3, nbins) float64 on the GPU: per scaled-value bin, the element count, the
+    sum of squared quantization errors and the same for an exact-scale reference."""
+    _gpu2d(x, "x")
+    rows, cols = x.shape
+    if out is None:
+        out = torch.empty((3, nbins), dtype=torch.float64, device=x.device)
+    cfg = make_config(block, True, False, rht, rht_mask, False, 0, 0, rule, scale_cap)
+    st = lib().nvfp4_error_stats(_ptr(x), _dtype_code(x), rows, cols, ctypes.byref(cfg), _ptr(amax_t), bin_width,
+                                 nbins, _ptr(out), _stream(x.device, stream))
+    _check(st, "nvfp4_error_stats")
     return out
 
 

@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <math.h>
+
 #include <type_traits>
 
 #include "nvfp4.h"
@@ -510,6 +512,94 @@ __global__ void tensor_scale_kernel(const float* __restrict__ amax, float cap6, 
   if (threadIdx.x == 0) out[0] = __fdiv_rn(amax[0], cap6);
 }
 
+// -------------------------------------------------------- error analysis ---
+
+// Per 16x16 region (16 lanes of a DPP row, one region row per lane): the
+// round-to-nearest quantization exactly as the quantize kernels compute it
+// (1x16 row blocks, optionally transformed, or one 16x16 tile), then per
+// element its scaled value z = fl(y * e) picks a bin, and the bin accumulates
+// the element count, eps^2 with eps = fl(y - fl(v * d)), and eps*^2 for the
+// reference that maps the block max exactly onto the chosen T (binary64):
+// v* = nearest-even E2M1 of T|y| / m, taken by comparing T|y| with the
+// midpoints times m (exact products), xh* = fl64(v* * m / T).
+constexpr int kMaxBins = 64;
+
+__device__ __forceinline__ double exact_scale_value(double ty, double m, const double* xs) {
+  // midpoints of the E2M1 grid; ties go to the even grid index
+  if (ty <= 0.25 * m) return 0.0;
+  if (ty < 0.75 * m) return xs[1];
+  if (ty <= 1.25 * m) return xs[2];
+  if (ty < 1.75 * m) return xs[3];
+  if (ty <= 2.5 * m) return xs[4];
+  if (ty < 3.5 * m) return xs[5];
+  if (ty <= 5.0 * m) return xs[6];
+  return xs[7];
+}
+
+template <int DT, bool RHT, bool TWO_D, int RULE>
+__global__ __launch_bounds__(kThreads) void err_stats_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                             QuantParams p, float inv_w, int nbins,
+                                                             double* __restrict__ stats) {
+  __shared__ f32x2 tab[128];
+  __shared__ double hist[3 * kMaxBins];
+  for (int k = threadIdx.x; k < 3 * nbins; k += kThreads) hist[k] = 0.0;
+  const TensorScale ts = workgroup_setup(p, tab);  // ends with a barrier
+  const int g = threadIdx.x >> 4, i = threadIdx.x & 15;
+  const int64_t rcols = cols / 16, nreg = (rows / 16) * rcols;
+  for (int64_t reg0 = (int64_t)blockIdx.x * 16; reg0 < nreg; reg0 += (int64_t)gridDim.x * 16) {
+    const int64_t reg = reg0 + g;
+    const bool active = reg < nreg;  // whole 16-lane groups
+    const int64_t rr = active ? reg / rcols : 0, cc = active ? reg - rr * rcols : 0;
+    float y[16];
+    load16<DT>(x, (rr * 16 + i) * cols + cc * 16, y);
+    if constexpr (RHT) rht16(y, p.rht_mask);
+    BlockResult res;
+    float m = absmax16(y);
+    if constexpr (TWO_D) {
+      res = quant_tile_row16<false, RULE>(y, nullptr, tab, ts.den6, ts.den4);
+      m = row16_max(m);
+    } else {
+      res = quant_block16<false, RULE>(y, nullptr, tab, ts.den6, ts.den4);
+    }
+    const float d = tab[res.sb].x;
+    f32x2 v[8];
+    v[0] = fp4_pair_values<0>(res.codes.lo);
+    v[1] = fp4_pair_values<1>(res.codes.lo);
+    v[2] = fp4_pair_values<2>(res.codes.lo);
+    v[3] = fp4_pair_values<3>(res.codes.lo);
+    v[4] = fp4_pair_values<0>(res.codes.hi);
+    v[5] = fp4_pair_values<1>(res.codes.hi);
+    v[6] = fp4_pair_values<2>(res.codes.hi);
+    v[7] = fp4_pair_values<3>(res.codes.hi);
+    const double T = res.four ? 4.0 : 6.0, md = (double)m;
+    double xs[8];
+    const double grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) xs[k] = (grid[k] * md) / T;
+    if (!active) continue;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float z = y[k] * res.e;
+      int b = (int)(fabsf(z) * inv_w);  // exact: inv_w is a power of two
+      b = b < nbins - 1 ? b : nbins - 1;
+      const float vk = (k & 1) ? v[k >> 1].y : v[k >> 1].x;
+      const float eps = y[k] - vk * d;
+      const double yd = (double)y[k];
+      const double xh = m != 0.0f ? exact_scale_value(T * fabs(yd), md, xs) : 0.0;
+      const double es = yd - copysign(xh, yd);
+      atomicAdd(&hist[b], 1.0);
+      atomicAdd(&hist[nbins + b], (double)eps * (double)eps);
+      atomicAdd(&hist[2 * nbins + b], es * es);
+    }
+  }
+  __syncthreads();
+  for (int k = threadIdx.x; k < 3 * nbins; k += kThreads) atomicAdd(&stats[k], hist[k]);
+}
+
+__global__ void zero_f64_kernel(double* __restrict__ p, int n) {
+  for (int k = threadIdx.x; k < n; k += blockDim.x) p[k] = 0.0;
+}
+
 // ------------------------------------------------------------ dequantize ---
 
 template <bool TWO_D>
@@ -861,6 +951,52 @@ nvfp4_status nvfp4_mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
   int64_t grid = (nblocks + kThreads - 1) / kThreads;
   if (grid > 65536) grid = 65536;
   hipLaunchKernelGGL(mx_dequant_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, codes, scales, nblocks, out);
+  return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+nvfp4_status nvfp4_error_stats(const void* x, nvfp4_dtype dtype, int64_t rows, int64_t cols, const nvfp4_config* cfg,
+                               const float* amax_dev, float bin_width, int32_t nbins, double* stats_dev,
+                               void* stream) {
+  if (!cfg || !amax_dev || !stats_dev) return NVFP4_ERR_NULL;
+  if (dtype != NVFP4_IN_BF16 && dtype != NVFP4_IN_F32) return NVFP4_ERR_DTYPE;
+  if (cfg->block != NVFP4_BLOCK_1D && cfg->block != NVFP4_BLOCK_2D) return NVFP4_ERR_UNSUPPORTED;
+  if (cfg->rule < NVFP4_RULE_NONE || cfg->rule > NVFP4_RULE_MAXERR) return NVFP4_ERR_UNSUPPORTED;
+  if (cfg->scale_cap != 448.0f && cfg->scale_cap != 256.0f) return NVFP4_ERR_UNSUPPORTED;
+  const bool two_d = cfg->block == NVFP4_BLOCK_2D;
+  if (cfg->sr || (cfg->rht && two_d)) return NVFP4_ERR_UNSUPPORTED;
+  if (nbins < 1 || nbins > kMaxBins) return NVFP4_ERR_UNSUPPORTED;
+  int ex = 0;
+  if (!(bin_width > 0.0f) || frexpf(bin_width, &ex) != 0.5f || ex < -100 || ex > 100) return NVFP4_ERR_UNSUPPORTED;
+  if (rows < 0 || cols < 0 || rows % 16 || cols % 16) return NVFP4_ERR_SHAPE;
+  const int64_t n = rows * cols;
+  if (n > 0 && !x) return NVFP4_ERR_NULL;
+  if (n > 0 && !aligned16(x)) return NVFP4_ERR_ALIGN;
+  QuantParams p{};
+  p.amax = amax_dev;
+  p.cap6 = 6.0f * cfg->scale_cap;
+  p.rht_mask = cfg->rht ? (cfg->rht_sign_mask & 0xFFFFu) : 0u;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(zero_f64_kernel, dim3(1), dim3(kThreads), 0, s, stats_dev, 3 * nbins);
+  const int64_t nreg = (rows / 16) * (cols / 16);
+  if (nreg > 0) {
+    const float inv_w = 1.0f / bin_width;  // exact: a power of two
+    const int64_t groups = (nreg + 15) / 16;
+    with_dtype(dtype, [&](auto DT) {
+      with_bool(cfg->rht != 0, [&](auto RHT) {
+        with_bool(two_d, [&](auto TWO_D) {
+          with_rule(cfg->rule, [&](auto RULE) {
+            if constexpr (!(RHT() && TWO_D())) {
+              auto k = err_stats_kernel<DT(), RHT(), TWO_D(), RULE()>;
+              int64_t grid = resident_grid(k);
+              if (grid > groups) grid = groups;
+              hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), 0, s, x, rows, cols, p, inv_w, nbins,
+                                 stats_dev);
+            }
+          });
+        });
+      });
+    });
+  }
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 

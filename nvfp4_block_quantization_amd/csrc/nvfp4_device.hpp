@@ -365,7 +365,8 @@ __device__ __forceinline__ Scale block_scale(float m, const Divisor& den, const 
 struct BlockResult {
   BlockCodes codes;
   uint32_t sb;
-  float e;  // reciprocal of the chosen candidate (reused to re-round the same values)
+  float e;            // reciprocal of the chosen candidate (reused to re-round the same values)
+  uint32_t four = 0;  // 1 when the scale-to-4 candidate was chosen
 };
 
 // One 16-element block held by one lane.  den6: fl(6 * S_t), den4: fl(4 * S_t).
@@ -393,7 +394,7 @@ __device__ __forceinline__ BlockResult quant_block16(const float* y, const uint3
     error_terms16<RULE>(y, c4, s4.d, t);
     const float err4 = reduce16<RULE>(t);
     const bool pick4 = err4 < err6;  // a tie keeps the scale-to-6 block
-    return pick4 ? BlockResult{c4, s4.sb, s4.e} : BlockResult{c6, s6.sb, s6.e};
+    return pick4 ? BlockResult{c4, s4.sb, s4.e, 1u} : BlockResult{c6, s6.sb, s6.e, 0u};
   }
 }
 
@@ -433,7 +434,7 @@ __device__ __forceinline__ BlockResult quant_tile_row16(const float* y, const ui
       err4 = row16_pairwise_sum(err4);
     }
     const bool pick4 = err4 < err6;
-    return pick4 ? BlockResult{c4, s4.sb, s4.e} : BlockResult{c6, s6.sb, s6.e};
+    return pick4 ? BlockResult{c4, s4.sb, s4.e, 1u} : BlockResult{c6, s6.sb, s6.e, 0u};
   }
 }
 

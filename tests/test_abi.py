@@ -113,3 +113,24 @@ def test_mxfp4_validation():
     assert L.nvfp4_mxfp4_dequantize(P(FAKE), P(FAKE), 32, 48, P(FAKE), None) == nv.ERR_SHAPE
     assert L.nvfp4_mxfp4_dequantize(None, P(FAKE), 32, 32, P(FAKE), None) == nv.ERR_NULL
     assert L.nvfp4_mxfp4_dequantize(P(FAKE), P(FAKE), 32, 32, P(FAKE + 4), None) == nv.ERR_ALIGN
+
+
+def test_error_stats_validation():
+    L = nv.lib()
+    P = ctypes.c_void_p
+
+    def es(rows=64, cols=64, cfg=None, w=0.25, nb=26, x=FAKE, amax=FAKE, out=FAKE):
+        cfg = cfg or nv.make_config()
+        return L.nvfp4_error_stats(P(x) if x else None, 0, rows, cols, ctypes.byref(cfg), P(amax) if amax else None,
+                                   w, nb, P(out) if out else None, None)
+    assert es(rows=8) == nv.ERR_SHAPE
+    assert es(cols=24) == nv.ERR_SHAPE
+    assert es(cfg=nv.make_config(sr=True)) == nv.ERR_UNSUPPORTED
+    assert es(cfg=nv.make_config(block="2d", rht=True)) == nv.ERR_UNSUPPORTED
+    assert es(w=0.3) == nv.ERR_UNSUPPORTED
+    assert es(w=0.0) == nv.ERR_UNSUPPORTED
+    assert es(nb=0) == nv.ERR_UNSUPPORTED
+    assert es(nb=65) == nv.ERR_UNSUPPORTED
+    assert es(out=0) == nv.ERR_NULL
+    assert es(amax=0) == nv.ERR_NULL
+    assert es(x=FAKE + 4) == nv.ERR_ALIGN
