@@ -82,6 +82,7 @@ def lib():
             "orc_mx_scale_code": (ctypes.c_uint8, [f32]),
             "orc_mxfp4_quantize": (i32, [P, i32, i64, i64, i32, i32, i32, u64, i64, P, P, P, P]),
             "orc_mxfp4_dequantize": (None, [P, P, i64, i64, P]),
+            "orc_gemm_fp4": (i32, [i32, P, P, f32, i32, P, P, f32, i32, i64, i64, i64, P, P]),
             "orc_error_stats": (i32, [P, i32, i64, i64, ctypes.POINTER(Config), f32, f32, i32, P]),
         }
         for name, (res, args) in sig.items():
@@ -293,3 +294,21 @@ def error_stats(x: np.ndarray, cfg: Config, a: float, bin_width: float = 0.25, n
     if rc != 0:
         raise ValueError(f"oracle rejected the error-analysis arguments (code {rc})")
     return out
+
+
+# ---- the consumer GEMM -------------------------------------------------------------
+
+def gemm_fp4(mx: bool, a_codes, a_scales, b_codes, b_scales, M: int, N: int, K: int, a_ts: float = 1.0,
+             b_ts: float = 1.0, a_2d: bool = False, b_2d: bool = False):
+    """C = A B^T on FP4 operands (float32 [M][N]) and sum |A B| (float64 [M][N])."""
+    ac = np.ascontiguousarray(a_codes, dtype=np.uint8)
+    asc = np.ascontiguousarray(a_scales, dtype=np.uint8)
+    bc = np.ascontiguousarray(b_codes, dtype=np.uint8)
+    bsc = np.ascontiguousarray(b_scales, dtype=np.uint8)
+    c = np.empty((M, N), np.float32)
+    cabs = np.empty((M, N), np.float64)
+    rc = lib().orc_gemm_fp4(int(mx), _ptr(ac), _ptr(asc), a_ts, int(a_2d), _ptr(bc), _ptr(bsc), b_ts, int(b_2d),
+                            M, N, K, _ptr(c), _ptr(cabs))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the GEMM shape (code {rc})")
+    return c, cabs

@@ -574,6 +574,48 @@ int orc_error_stats(const void* x, int dtype, int64_t rows, int64_t cols, const 
 }
 
 /* ------------------------------------------------------------------------ */
+/* The consumer: a GEMM on block-scaled FP4 operands                          */
+/* ------------------------------------------------------------------------ */
+
+/* The value an operand element encodes, exactly (binary64 holds it):
+ * NVFP4: v(code) * dec(sb), the tensor scale applied once to the whole product;
+ * MXFP4: v(code) * 2^(sc - 127). */
+static double nv_elem(const uint8_t* codes, const uint8_t* scales, int block_2d, int64_t r, int64_t k, int64_t K) {
+  uint8_t byte = codes[r * (K / 2) + k / 2];
+  uint8_t c = (k & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+  uint8_t sb = block_2d ? scales[(r / 16) * (K / 16) + k / 16] : scales[r * (K / 16) + k / 16];
+  return (double)orc_e2m1_value(c) * (double)orc_e4m3_value(sb);
+}
+
+static double mx_elem(const uint8_t* codes, const uint8_t* scales, int64_t r, int64_t k, int64_t K) {
+  uint8_t byte = codes[r * (K / 2) + k / 2];
+  uint8_t c = (k & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+  return (double)orc_e2m1_value(c) * (double)orc_e8m0_value(scales[r * (K / 32) + k / 32]);
+}
+
+int orc_gemm_fp4(int mx, const uint8_t* a_codes, const uint8_t* a_scales, float a_ts, int a_2d, const uint8_t* b_codes,
+                 const uint8_t* b_scales, float b_ts, int b_2d, int64_t M, int64_t N, int64_t K, float* c,
+                 double* c_abs) {
+  if (M < 0 || N < 0 || K < 0 || K % (mx ? 32 : 16)) return 1;
+  if (!mx && ((a_2d && M % 16) || (b_2d && N % 16))) return 1;
+  const double ts = mx ? 1.0 : (double)a_ts * (double)b_ts;
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t n = 0; n < N; ++n) {
+      double acc = 0.0, aacc = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        double a = mx ? mx_elem(a_codes, a_scales, m, k, K) : nv_elem(a_codes, a_scales, a_2d, m, k, K);
+        double b = mx ? mx_elem(b_codes, b_scales, n, k, K) : nv_elem(b_codes, b_scales, b_2d, n, k, K);
+        acc += a * b; /* each product is exact in binary64 */
+        aacc += fabs(a * b);
+      }
+      c[m * N + n] = (float)(acc * ts);
+      if (c_abs) c_abs[m * N + n] = aacc * fabs(ts);
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* MXFP4: 32-element blocks with power-of-two (E8M0) scales                   */
 /* ------------------------------------------------------------------------ */
 

@@ -38,6 +38,8 @@
  *   orc_e2m1_sr -- pinned statistically (unbiasedness) and by its special
  *       cases; the exact random-word-to-decision mapping is a reading, not a
  *       page fact.
+ *   orc_gemm_fp4 -- pinned by numpy float64 matrix products of operands
+ *       decoded through the pinned format functions, and closed forms.
  *   orc_error_stats -- pinned by the total squared error of orc_quantize +
  *       orc_dequantize, brute-force exact-scale rounding with rationals, and
  *       the concentration of error near the scaled value 5 that [P2]
@@ -128,6 +130,21 @@ void orc_dequantize(const uint8_t* codes, const uint8_t* scales, float tensor_sc
  * rows % 16 == 0, cols % 16 == 0, 1 <= nbins <= 64, no stochastic rounding. */
 int orc_error_stats(const void* x, int dtype, int64_t rows, int64_t cols, const orc_config* cfg, float amax,
                     float bin_width, int nbins, double* stats);
+
+/* ---- the consumer: GEMM on FP4 operands ([P4], the news page "NVFP4
+ * revolutionizes AI training" (title translated): the format exists for fast
+ * FP4 matrix products) ----------------------------------------------------
+ * C[m][n] = sum_k A[m][k] * B[n][k] ("NT": both operands stored with K
+ * contiguous, as quantized row copies), where an operand element is the value
+ * its encoding stands for: NVFP4 v * dec(sb) * S_t (scales [rows][K/16], or
+ * [rows/16][K/16] for 16x16 tiles), MXFP4 v * 2^(sc - 127) (scales [rows][K/32]).
+ * Products are exact in binary64 and summed in k order in binary64; the tensor
+ * scales multiply the sum; one rounding to binary32 at the end.  c_abs (may be
+ * NULL) receives sum_k |A B| (with the tensor scales), for error bounds.
+ * mx = 1: MXFP4 operands (a_ts, b_ts, a_2d, b_2d ignored). */
+int orc_gemm_fp4(int mx, const uint8_t* a_codes, const uint8_t* a_scales, float a_ts, int a_2d, const uint8_t* b_codes,
+                 const uint8_t* b_scales, float b_ts, int b_2d, int64_t M, int64_t N, int64_t K, float* c,
+                 double* c_abs);
 
 /* ---- MXFP4 (the contrast format of [P1] section 1) ----------------------
  * OCP Microscaling (MX) FP4: 32-element row blocks, each with a power-of-two
