@@ -222,6 +222,34 @@ nvfp4_status nvfp4_mxfp4_quantize(const void* x, nvfp4_dtype dtype, int64_t rows
 nvfp4_status nvfp4_mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                                     float* out, void* stream);
 
+/* ---- the consumer: FP4 GEMM ---------------------------------------------------
+ * [P4] (the news page "NVFP4 revolutionizes AI training", title translated)
+ * gives fast FP4 matrix products as the reason for the format.  Both calls
+ * compute C = A B^T from quantized row copies with K contiguous ("NT"):
+ *   A codes [M][K/2], B codes [N][K/2] (as written by the quantize calls),
+ *   C float [M][N] row-major, overwritten.
+ * The result is the value the operands encode, summed with fp32 accumulation
+ * on the matrix cores: each instruction adds its exact products to the running
+ * sum with at most one unit of 2^-24 of (|running sum| + sum |products|) of
+ * error (measured), so |C - exact| <= 2 (K / k_i) 2^-24 sum_k |A B|, with k_i =
+ * 64 values per instruction for MXFP4 and 16 for NVFP4 (plus one unit of |C|
+ * for NVFP4's tensor-scale multiply).  Deterministic run to run.
+ * Pointers: codes 16-byte aligned, scales and C 4-byte aligned.
+ *
+ * NVFP4: scales [M][K/16] / [N][K/16] (NVFP4_BLOCK_1D) or [M/16][K/16] /
+ *   [N/16][K/16] (NVFP4_BLOCK_2D, e.g. the column copy of a 16x16-tiled weight);
+ *   a_tensor_scale, b_tensor_scale: device floats.  K % 64 == 0; M % 16 == 0 with
+ *   2D A, N % 16 == 0 with 2D B.  C = S_tA S_tB sum_k (v dec(sb))_A (v dec(sb))_B. */
+nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
+                        nvfp4_block a_block, const uint8_t* b_codes, const uint8_t* b_scales,
+                        const float* b_tensor_scale, nvfp4_block b_block, int64_t M, int64_t N, int64_t K, float* c,
+                        void* stream);
+
+/* MXFP4: scales [M][K/32] and [N][K/32] (E8M0); K % 128 == 0.
+ * C = sum_k v_A 2^(sA - 127) v_B 2^(sB - 127). */
+nvfp4_status nvfp4_mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                              const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, float* c, void* stream);
+
 const char* nvfp4_status_string(nvfp4_status s);
 int nvfp4_abi_version(void);
 

@@ -100,6 +100,10 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_error_stats.restype = i32
         L.nvfp4_error_stats.argtypes = [P, i32, i64, i64, ctypes.POINTER(Config), P, ctypes.c_float, ctypes.c_int32,
                                         P, P]
+        L.nvfp4_gemm.restype = i32
+        L.nvfp4_gemm.argtypes = [P, P, P, i32, P, P, P, i32, i64, i64, i64, P, P]
+        L.nvfp4_mxfp4_gemm.restype = i32
+        L.nvfp4_mxfp4_gemm.argtypes = [P, P, P, P, i64, i64, i64, P, P]
         L.nvfp4_mxfp4_quantize.restype = i32
         L.nvfp4_mxfp4_quantize.argtypes = [P, i32, i64, i64, ctypes.POINTER(MXConfig), ctypes.POINTER(MXOutputs), P]
         L.nvfp4_mxfp4_dequantize.restype = i32
@@ -275,4 +279,42 @@ def mxfp4_dequantize(codes: torch.Tensor, scales: torch.Tensor, rows: int, cols:
     st = lib().nvfp4_mxfp4_dequantize(_ptr(codes), _ptr(scales), rows, cols, _ptr(out),
                                       _stream(codes.device, stream))
     _check(st, "nvfp4_mxfp4_dequantize")
+    return out
+
+
+# ---- the consumer: FP4 GEMM (C = A B^T, operands with K contiguous) ------------
+
+def gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, a_tensor_scale: torch.Tensor, b_codes: torch.Tensor,
+         b_scales: torch.Tensor, b_tensor_scale: torch.Tensor, a_block: str = "1d", b_block: str = "1d",
+         out: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """float32 [M][N] = A B^T from NVFP4 row copies (codes [M][K/2], [N][K/2])."""
+    _gpu2d(a_codes, "a_codes")
+    _gpu2d(b_codes, "b_codes")
+    M, K = a_codes.shape[0], 2 * a_codes.shape[1]
+    N = b_codes.shape[0]
+    if 2 * b_codes.shape[1] != K:
+        raise ValueError("A and B must have the same K")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a_codes.device)
+    st = lib().nvfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(a_tensor_scale), BLOCKS[a_block], _ptr(b_codes),
+                          _ptr(b_scales), _ptr(b_tensor_scale), BLOCKS[b_block], M, N, K, _ptr(out),
+                          _stream(a_codes.device, stream))
+    _check(st, "nvfp4_gemm")
+    return out
+
+
+def mxfp4_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor, b_scales: torch.Tensor,
+               out: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """float32 [M][N] = A B^T from MXFP4 row copies (codes [M][K/2], [N][K/2])."""
+    _gpu2d(a_codes, "a_codes")
+    _gpu2d(b_codes, "b_codes")
+    M, K = a_codes.shape[0], 2 * a_codes.shape[1]
+    N = b_codes.shape[0]
+    if 2 * b_codes.shape[1] != K:
+        raise ValueError("A and B must have the same K")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a_codes.device)
+    st = lib().nvfp4_mxfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), M, N, K, _ptr(out),
+                                _stream(a_codes.device, stream))
+    _check(st, "nvfp4_mxfp4_gemm")
     return out

@@ -1,4 +1,5 @@
-"""Build libnvfp4.so (gfx950) in-tree with hipcc."""
+"""Build libnvfp4.so (gfx950) in-tree with hipcc: the quantization kernels
+(csrc/nvfp4.hip) and the FP4 GEMM consumer (csrc/gemm.hip)."""
 from __future__ import annotations
 
 import os
@@ -7,7 +8,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = [os.path.join(HERE, "csrc", "nvfp4.hip")]
+SOURCES = [os.path.join(HERE, "csrc", "nvfp4.hip"), os.path.join(HERE, "csrc", "gemm.hip")]
 LIB = os.path.join(HERE, "libnvfp4.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -134,3 +134,24 @@ def test_error_stats_validation():
     assert es(out=0) == nv.ERR_NULL
     assert es(amax=0) == nv.ERR_NULL
     assert es(x=FAKE + 4) == nv.ERR_ALIGN
+
+
+def test_gemm_validation():
+    L = nv.lib()
+    P = ctypes.c_void_p
+    f = P(FAKE)
+
+    def g(M=64, N=64, K=128, ab=0, bb=0, ac=FAKE, c=FAKE):
+        return L.nvfp4_gemm(P(ac) if ac else None, f, f, ab, f, f, f, bb, M, N, K, P(c) if c else None, None)
+    assert g(K=96) == nv.ERR_SHAPE
+    assert g(M=8, ab=1) == nv.ERR_SHAPE
+    assert g(N=24, bb=1) == nv.ERR_SHAPE
+    assert g(ab=3) == nv.ERR_UNSUPPORTED
+    assert g(c=0) == nv.ERR_NULL
+    assert g(ac=0) == nv.ERR_NULL
+    assert g(ac=FAKE + 8) == nv.ERR_ALIGN
+    assert g(c=FAKE + 2) == nv.ERR_ALIGN
+    assert g(M=0) == nv.OK
+    assert L.nvfp4_mxfp4_gemm(f, f, f, f, 64, 64, 192, f, None) == nv.ERR_SHAPE
+    assert L.nvfp4_mxfp4_gemm(None, f, f, f, 64, 64, 256, f, None) == nv.ERR_NULL
+    assert L.nvfp4_mxfp4_gemm(f, f, P(FAKE + 4), f, 64, 64, 256, f, None) == nv.ERR_ALIGN
