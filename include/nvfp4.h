@@ -238,7 +238,7 @@ nvfp4_status nvfp4_mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
  *
  * NVFP4: scales [M][K/16] / [N][K/16] (NVFP4_BLOCK_1D) or [M/16][K/16] /
  *   [N/16][K/16] (NVFP4_BLOCK_2D, e.g. the column copy of a 16x16-tiled weight);
- *   a_tensor_scale, b_tensor_scale: device floats.  K % 64 == 0; M % 16 == 0 with
+ *   a_tensor_scale, b_tensor_scale: device floats.  K % 128 == 0; M % 16 == 0 with
  *   2D A, N % 16 == 0 with 2D B.  C = S_tA S_tB sum_k (v dec(sb))_A (v dec(sb))_B. */
 nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
                         nvfp4_block a_block, const uint8_t* b_codes, const uint8_t* b_scales,

@@ -20,13 +20,17 @@
 // assignment of K values to the two lane halves gives the same sum, so each
 // half here walks its own contiguous K range and loads whole 16-byte pieces.
 //
-// Tiling: a workgroup of 4 waves owns a 128x128 tile of C, each wave a 64x64
-// quarter (2x2 instruction tiles); operand fragments come straight from
+// Tiling (MXFP4): 256x256 workgroup tiles staged through an LDS ring, below.
+// Tiling (NVFP4): a workgroup of 4 waves owns a 128x128 tile of C, each wave a
+// 64x64 quarter (2x2 instruction tiles); operand fragments come straight from
 // global memory (each 16-byte piece feeds two instructions of the wave and the
 // neighbouring waves hit it in L2), with the next K step's fragments loaded
-// while the current step's instructions run.
+// while the current step's instructions run, and are expanded to fp16 in
+// registers.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "nvfp4.h"
 
@@ -36,9 +40,9 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: stays in registers
 
 constexpr int kThreads = 256;
-constexpr int kTile = 128;  // workgroup tile of C (M and N)
 
 // Dispatch order: consecutive workgroups go round-robin over the 8 XCDs; give
 // each XCD one contiguous range of tiles (N fastest), so the tiles that share
@@ -62,142 +66,192 @@ __device__ __forceinline__ void store_tile(float* __restrict__ C, int64_t M, int
 
 // ------------------------------------------------------------------ MXFP4 ---
 
-struct MxFrag {
-  uint4 q[4];   // 4 x 32 FP4 values: K [kb + 32 c, +32) for c = 0..3
-  uint32_t s;   // their 4 E8M0 scales, byte c for chunk c
+// MXFP4: a workgroup of 4 waves owns a 256x256 tile of C, each wave a 128x128
+// quarter (4x4 instruction tiles, 256 fp32 accumulators per lane).  Per
+// 128-value K step the workgroup's 256 A rows and 256 B rows (64 bytes each)
+// and their scale words are staged in LDS; every 16-byte operand piece read
+// from LDS feeds four instructions.  LDS pieces are XOR-swizzled by row so that
+// the 16 lanes of a read phase hit distinct banks.
+constexpr int kBig = 256;  // workgroup tile (M and N)
+constexpr int kStepK = 128;
+
+struct MxStage {
+  u32x4 a[kBig * 4];  // 256 rows x 4 pieces of 16 bytes (32 FP4 values each)
+  u32x4 b[kBig * 4];
+  uint32_t sa[kBig];  // 4 E8M0 scales per row (the step's four 32-value blocks)
+  uint32_t sb[kBig];
 };
 
-__device__ __forceinline__ void mx_load(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-                                        int64_t row, int64_t K, int64_t kb, MxFrag& f) {
-  const uint8_t* p = codes + row * (K / 2) + kb / 2;
-  const uint8_t* ps = scales + row * (K / 32) + kb / 32;
-  if (kb + 128 <= K) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) f.q[c] = reinterpret_cast<const uint4*>(p)[c];
-    f.s = *reinterpret_cast<const uint32_t*>(ps);  // kb is a multiple of 128: 4-byte aligned
-  } else {  // K tail: missing 32-value chunks are zero (scale 2^0)
-    f.s = 0x7F7F7F7Fu;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if (kb + 32 * c < K) {
-        f.q[c] = reinterpret_cast<const uint4*>(p)[c];
-        f.s = (f.s & ~(0xFFu << (8 * c))) | ((uint32_t)ps[c] << (8 * c));
-      } else {
-        f.q[c] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  }
+__device__ __forceinline__ int piece_slot(int row, int part) { return row * 4 + (part ^ ((row >> 2) & 3)); }
+
+// Grouped raster: 4 tile rows per group, columns outer, so the workgroups that
+// run together on one XCD share A tiles (4 rows) and B tiles (consecutive columns).
+__device__ __forceinline__ void grouped_tile(uint32_t L, uint32_t tiles_m, uint32_t tiles_n, uint32_t& tm,
+                                             uint32_t& tn) {
+  constexpr uint32_t G = 4;
+  const uint32_t group = L / (G * tiles_n), first = group * G;
+  const uint32_t gsize = tiles_m - first < G ? tiles_m - first : G;
+  const uint32_t in = L - group * G * tiles_n;
+  tm = first + in % gsize;
+  tn = in / gsize;
 }
 
 template <int C>
-__device__ __forceinline__ v16f mx_mfma(const MxFrag& a, const MxFrag& b, v16f acc) {
-  const v8i va = {(int)a.q[C].x, (int)a.q[C].y, (int)a.q[C].z, (int)a.q[C].w, 0, 0, 0, 0};
-  const v8i vb = {(int)b.q[C].x, (int)b.q[C].y, (int)b.q[C].z, (int)b.q[C].w, 0, 0, 0, 0};
-  // formats 4/4: E2M1 x E2M1; scale byte C of each lane's scale word
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, vb, acc, 4, 4, C, (int)a.s, C, (int)b.s);
+__device__ __forceinline__ v16f mx_mfma_s(u32x4 a, u32x4 b, uint32_t sa, uint32_t sb, v16f acc) {
+  const v8i va = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const v8i vb = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, vb, acc, 4, 4, 2 * C, (int)sa, 2 * C, (int)sb);
 }
 
-__global__ __launch_bounds__(kThreads) void mx_gemm_kernel(const uint8_t* __restrict__ A,
-                                                           const uint8_t* __restrict__ As,
-                                                           const uint8_t* __restrict__ B,
-                                                           const uint8_t* __restrict__ Bs, int64_t M, int64_t N,
-                                                           int64_t K, float* __restrict__ C, uint32_t tiles_n) {
-  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, h = l >> 5;
-  const uint32_t tile = xcd_tile(blockIdx.x, gridDim.x);
-  const uint32_t tm = tile / tiles_n, tn = tile - tm * tiles_n;
-  const int64_t m0 = (int64_t)tm * kTile + 64 * (wave >> 1), n0 = (int64_t)tn * kTile + 64 * (wave & 1);
-  int64_t ra[2], rb[2];
+// One 64-value chunk (c = 0, 1) of a K step: 4 A and 4 B pieces from LDS, 16 instructions.
+// Operand pieces of one 64-value chunk (CH = 0, 1) of a K step, from LDS.
+template <int CH>
+__device__ __forceinline__ void mx_read(const MxStage& s, int wr, int wc, int l, int h, u32x4 (&fa)[4],
+                                        u32x4 (&fb)[4]) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int64_t r = m0 + 32 * i + (l & 31), s = n0 + 32 * i + (l & 31);
-    ra[i] = r < M ? r : M - 1;  // rows past the edge load a valid row; their results are not stored
-    rb[i] = s < N ? s : N - 1;
+  for (int i = 0; i < 4; ++i) {
+    fa[i] = s.a[piece_slot(wr + 32 * i + (l & 31), 2 * CH + h)];
+    fb[i] = s.b[piece_slot(wc + 32 * i + (l & 31), 2 * CH + h)];
   }
-  v16f acc[2][2];
+}
+
+// The 16 instructions of one chunk: every A piece meets every B piece.
+template <int CH>
+__device__ __forceinline__ void mx_mma(const u32x4 (&fa)[4], const u32x4 (&fb)[4], const uint32_t (&sa)[4],
+                                       const uint32_t (&sb)[4], v16f (&acc)[4][4]) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j) acc[i][j] = mx_mfma_s<CH>(fa[i], fb[j], sa[i], sb[j], acc[i][j]);
+}
+
+__device__ __forceinline__ void mx_read_scales(const MxStage& s, int wr, int wc, int l, int h, uint32_t (&sa)[4],
+                                               uint32_t (&sb)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sa[i] = s.sa[wr + 32 * i + (l & 31)] >> (8 * h);  // lane half h: blocks 2c + h -> byte 2c
+    sb[i] = s.sb[wc + 32 * i + (l & 31)] >> (8 * h);
+  }
+}
+
+// The operands travel from memory straight into a ring of four LDS stages
+// (global_load_lds, no staging registers), three K steps ahead of the step
+// being computed.  The barrier that publishes a stage waits only for that
+// stage's loads (vmcnt counts the two younger steps' loads as still pending).
+constexpr int kRing = 4;
+
+// s_waitcnt immediate: vector-memory count <= N, LDS/scalar count 0 (gfx9 encoding)
+#define MX_WAIT_VM_LGKM0(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (0 << 8) | (((N) >> 4) << 14))
+
+__global__ __launch_bounds__(kThreads) void mx_gemm_dma_kernel(const uint8_t* __restrict__ A,
+                                                               const uint8_t* __restrict__ As,
+                                                               const uint8_t* __restrict__ B,
+                                                               const uint8_t* __restrict__ Bs, int64_t M, int64_t N,
+                                                               int64_t K, float* __restrict__ C, uint32_t tiles_m,
+                                                               uint32_t tiles_n) {
+  __shared__ MxStage st[kRing];
+  const int t = threadIdx.x, wave = t >> 6, l = t & 63, h = l >> 5;
+  uint32_t tm, tn;
+  grouped_tile(xcd_tile(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+  const int64_t am0 = (int64_t)tm * kBig, bn0 = (int64_t)tn * kBig;
+  const int64_t kbytes = K / 2;
+
+  // Load j of thread t fills LDS slot p = t + 256 j, i.e. row p / 4 = t / 4 + 64 j and
+  // stored part t % 4, which holds the operand piece part (t % 4) ^ swizzle(row).
+  int64_t offa[4], offb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (t >> 2) + 64 * j;
+    const int part = (t & 3) ^ ((row >> 2) & 3);
+    const int64_t ar = am0 + row, br = bn0 + row;
+    offa[j] = (ar < M ? ar : M - 1) * kbytes + 16 * part;  // rows past the edge load a valid row
+    offb[j] = (br < N ? br : N - 1) * kbytes + 16 * part;
+  }
+  const int64_t sar = am0 + t < M ? am0 + t : M - 1, sbr = bn0 + t < N ? bn0 + t : N - 1;
+  const uint8_t* gsa = As + sar * (K / 32);
+  const uint8_t* gsb = Bs + sbr * (K / 32);
+  const int wbase = 64 * wave;  // first slot (and scale row) this wave's loads fill
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  MxFrag fa[2][2], fb[2][2];  // [buffer][tile]
-  auto load = [&](int buf, int64_t k0) {
-    const int64_t kb = k0 + 128 * h;
+  const int wr = 128 * (wave >> 1), wc = 128 * (wave & 1);  // this wave's quarter of the tile
+  const int64_t nsteps = K / kStepK, last = nsteps - 1;
+  // 10 loads per step and thread; past the last step they re-read the last step
+  auto issue = [&](int64_t step) {
+    const int64_t st_ = step < last ? step : last;
+    MxStage& d = st[step & (kRing - 1)];
+    const int64_t kb = st_ * (kStepK / 2);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      mx_load(A, As, ra[i], K, kb, fa[buf][i]);
-      mx_load(B, Bs, rb[i], K, kb, fb[buf][i]);
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_global_load_lds(A + offa[j] + kb, &d.a[256 * j + wbase], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(B + offb[j] + kb, &d.b[256 * j + wbase], 16, 0, 0);
     }
+    __builtin_amdgcn_global_load_lds(gsa + st_ * (kStepK / 32), &d.sa[wbase], 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(gsb + st_ * (kStepK / 32), &d.sb[wbase], 4, 0, 0);
   };
-  auto step = [&](int buf) {
+  issue(0);
+  issue(1);
+  issue(2);
+  MX_WAIT_VM_LGKM0(20);  // step 0 landed (steps 1 and 2 may be pending)
+  __builtin_amdgcn_s_barrier();
+
+  u32x4 f0a[4], f0b[4], f1a[4], f1b[4];
+  uint32_t sa[4], sb[4], nsa[4], nsb[4];
+  mx_read<0>(st[0], wr, wc, l, h, f0a, f0b);
+  mx_read_scales(st[0], wr, wc, l, h, sa, sb);
+  for (int64_t s = 0; s < nsteps; ++s) {
+    const MxStage& cur = st[s & (kRing - 1)];
+    const MxStage& nxt = st[(s + 1) & (kRing - 1)];
+    mx_read<1>(cur, wr, wc, l, h, f1a, f1b);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_mma<0>(f0a, f0b, sa, sb, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(s + 3);          // into stage (s + 3) % 4 = (s - 1) % 4, read by every wave before the last barrier
+    MX_WAIT_VM_LGKM0(20);  // this thread's loads of step s + 1 have landed; steps s + 2, s + 3 pending
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    mx_read<0>(nxt, wr, wc, l, h, f0a, f0b);
+    mx_read_scales(nxt, wr, wc, l, h, nsa, nsb);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_mma<1>(f1a, f1b, sa, sb, acc);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        acc[i][j] = mx_mfma<0>(fa[buf][i], fb[buf][j], acc[i][j]);
-        acc[i][j] = mx_mfma<1>(fa[buf][i], fb[buf][j], acc[i][j]);
-        acc[i][j] = mx_mfma<2>(fa[buf][i], fb[buf][j], acc[i][j]);
-        acc[i][j] = mx_mfma<3>(fa[buf][i], fb[buf][j], acc[i][j]);
-      }
-  };
-  load(0, 0);
-  for (int64_t k0 = 0; k0 < K; k0 += 512) {
-    if (k0 + 256 < K) load(1, k0 + 256);
-    step(0);
-    if (k0 + 256 >= K) break;
-    if (k0 + 512 < K) load(0, k0 + 512);
-    step(1);
+    for (int i = 0; i < 4; ++i) {
+      sa[i] = nsa[i];
+      sb[i] = nsb[i];
+    }
   }
+  MX_WAIT_VM_LGKM0(0);  // no load may still be writing LDS when the workgroup ends
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) store_tile(C, M, N, m0 + 32 * i, n0 + 32 * j, acc[i][j], l, 1.0f);
+    for (int j = 0; j < 4; ++j) store_tile(C, M, N, am0 + wr + 32 * i, bn0 + wc + 32 * j, acc[i][j], l, 1.0f);
 }
+#undef MX_WAIT_VM_LGKM0
 
 // ------------------------------------------------------------------ NVFP4 ---
 
-struct NvFrag {
-  uint4 q[2];  // 64 FP4 values: K [kb, kb + 64)
-  uint32_t s;  // E4M3 scales of the four 16-value blocks
+// Same workgroup tiling and LDS ring as MXFP4.  Per 128-value K step a row
+// brings 64 code bytes (four 16-byte pieces) and eight E4M3 scales (two scale
+// words); each 16-value block becomes fp16 operands in registers: the code
+// converts exactly to fp16, times its block scale (exact: at most 6 significant
+// bits), and the fp16 instruction 32x32x16 takes 8 values per lane.  Lane half
+// h walks K values [64 h, 64 h + 64) of the step: pieces 2h and 2h + 1.
+struct NvStage {
+  u32x4 a[kBig * 4];
+  u32x4 b[kBig * 4];
+  uint32_t sa[2][kBig];  // scale words: [0] blocks 0-3 of the step, [1] blocks 4-7
+  uint32_t sb[2][kBig];
 };
 
-__device__ __forceinline__ void nv_load(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-                                        int64_t row, int64_t srow, int64_t K, int64_t kb, NvFrag& f) {
-  const uint8_t* p = codes + row * (K / 2) + kb / 2;
-  const uint8_t* ps = scales + srow * (K / 16) + kb / 16;
-  if (kb + 64 <= K) {
-    f.q[0] = reinterpret_cast<const uint4*>(p)[0];
-    f.q[1] = reinterpret_cast<const uint4*>(p)[1];
-    f.s = *reinterpret_cast<const uint32_t*>(ps);  // kb is a multiple of 64: 4-byte aligned
-  } else {  // K tail in 16-value blocks: missing blocks are zero
-    uint32_t w[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) w[c] = kb + 8 * c < K ? reinterpret_cast<const uint32_t*>(p)[c] : 0u;
-    f.q[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    f.q[1] = make_uint4(w[4], w[5], w[6], w[7]);
-    f.s = 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (kb + 16 * c < K) f.s |= (uint32_t)ps[c] << (8 * c);
-  }
-}
-
-// fp16 operand for K values [kb + 8 c, +8): codes word c, scale of block c / 2.
-template <int C>
-__device__ __forceinline__ v8h nv_half8(const NvFrag& f, const h2 sc2[4]) {
-  const uint32_t w = C < 4 ? (C == 0 ? f.q[0].x : C == 1 ? f.q[0].y : C == 2 ? f.q[0].z : f.q[0].w)
-                           : (C == 4 ? f.q[1].x : C == 5 ? f.q[1].y : C == 6 ? f.q[1].z : f.q[1].w);
-  const h2 s = sc2[C >> 1];
-  const h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
-  const h2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
-  const h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
-  const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
-  return v8h{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-}
-
-// The four E4M3 block scales as fp16 pairs (exact: E4M3 lies inside fp16).
-__device__ __forceinline__ void nv_scales(uint32_t s, h2 out[4]) {
+// The four E4M3 scales of a word as fp16 pairs (exact: E4M3 lies inside fp16).
+__device__ __forceinline__ void nv_scales(uint32_t s, h2 (&out)[4]) {
   typedef float f2 __attribute__((ext_vector_type(2)));
   const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(s, false);  // bytes 0, 1
   const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(s, true);   // bytes 2, 3
@@ -208,9 +262,19 @@ __device__ __forceinline__ void nv_scales(uint32_t s, h2 out[4]) {
   out[3] = h2{v3, v3};
 }
 
-template <int C>
-__device__ __forceinline__ v16f nv_mfma(const NvFrag& a, const h2 sa[4], const NvFrag& b, const h2 sb[4], v16f acc) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(nv_half8<C>(a, sa), nv_half8<C>(b, sb), acc, 0, 0, 0);
+// 8 codes (one word) times their block scale, as an fp16 operand.
+__device__ __forceinline__ v8h nv_half8(uint32_t w, h2 s) {
+  const h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
+  const h2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
+  const h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
+  const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
+  return v8h{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+__device__ __forceinline__ uint32_t word_of(const u32x4 (&q)[2], int c) {
+  const u32x4 v = q[c >> 2];
+  const int k = c & 3;
+  return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
 }
 
 template <bool A2D, bool B2D>
@@ -220,76 +284,116 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(const uint8_t* __rest
                                                            const uint8_t* __restrict__ B,
                                                            const uint8_t* __restrict__ Bs,
                                                            const float* __restrict__ bts, int64_t M, int64_t N,
-                                                           int64_t K, float* __restrict__ C, uint32_t tiles_n) {
-  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, h = l >> 5;
-  const uint32_t tile = xcd_tile(blockIdx.x, gridDim.x);
-  const uint32_t tm = tile / tiles_n, tn = tile - tm * tiles_n;
-  const int64_t m0 = (int64_t)tm * kTile + 64 * (wave >> 1), n0 = (int64_t)tn * kTile + 64 * (wave & 1);
-  int64_t ra[2], rb[2], sa_row[2], sb_row[2];
+                                                           int64_t K, float* __restrict__ C, uint32_t tiles_m,
+                                                           uint32_t tiles_n) {
+  __shared__ NvStage st[kRing];
+  const int t = threadIdx.x, wave = t >> 6, l = t & 63, h = l >> 5;
+  uint32_t tm, tn;
+  grouped_tile(xcd_tile(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+  const int64_t am0 = (int64_t)tm * kBig, bn0 = (int64_t)tn * kBig;
+  const int64_t kbytes = K / 2;
+
+  int64_t offa[4], offb[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int64_t r = m0 + 32 * i + (l & 31), s = n0 + 32 * i + (l & 31);
-    ra[i] = r < M ? r : M - 1;
-    rb[i] = s < N ? s : N - 1;
-    sa_row[i] = A2D ? ra[i] / 16 : ra[i];
-    sb_row[i] = B2D ? rb[i] / 16 : rb[i];
+  for (int j = 0; j < 4; ++j) {
+    const int row = (t >> 2) + 64 * j;
+    const int part = (t & 3) ^ ((row >> 2) & 3);
+    const int64_t ar = am0 + row, br = bn0 + row;
+    offa[j] = (ar < M ? ar : M - 1) * kbytes + 16 * part;
+    offb[j] = (br < N ? br : N - 1) * kbytes + 16 * part;
   }
-  v16f acc[2][2];
+  int64_t sar = am0 + t < M ? am0 + t : M - 1, sbr = bn0 + t < N ? bn0 + t : N - 1;
+  if (A2D) sar /= 16;
+  if (B2D) sbr /= 16;
+  const uint8_t* gsa = As + sar * (K / 16);
+  const uint8_t* gsb = Bs + sbr * (K / 16);
+  const int wbase = 64 * wave;
+
+  v16f acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  NvFrag fa[2][2], fb[2][2];
-  auto load = [&](int buf, int64_t k0) {
-    const int64_t kb = k0 + 64 * h;
+  const int wr = 128 * (wave >> 1), wc = 128 * (wave & 1);
+  const int64_t nsteps = K / kStepK, last = nsteps - 1;
+  auto issue = [&](int64_t step) {  // 12 loads per step and thread
+    const int64_t st_ = step < last ? step : last;
+    NvStage& d = st[step & (kRing - 1)];
+    const int64_t kb = st_ * (kStepK / 2);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      nv_load(A, As, ra[i], sa_row[i], K, kb, fa[buf][i]);
-      nv_load(B, Bs, rb[i], sb_row[i], K, kb, fb[buf][i]);
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_global_load_lds(A + offa[j] + kb, &d.a[256 * j + wbase], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(B + offb[j] + kb, &d.b[256 * j + wbase], 16, 0, 0);
+    }
+    const int64_t ks = st_ * (kStepK / 16);  // 8 scale bytes per row and step
+    __builtin_amdgcn_global_load_lds(gsa + ks, &d.sa[0][wbase], 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(gsa + ks + 4, &d.sa[1][wbase], 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(gsb + ks, &d.sb[0][wbase], 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(gsb + ks + 4, &d.sb[1][wbase], 4, 0, 0);
+  };
+#define NV_WAIT_VM_LGKM0(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (0 << 8) | (((N) >> 4) << 14))
+  issue(0);
+  issue(1);
+  issue(2);
+  NV_WAIT_VM_LGKM0(24);
+  __builtin_amdgcn_s_barrier();
+
+  // this lane's code pieces (2 per tile) and scale words of the current step
+  u32x4 qa[4][2], qb[4][2];
+  uint32_t wsa[4], wsb[4];
+  auto read_step = [&](const NvStage& s) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ra = wr + 32 * i + (l & 31), rb = wc + 32 * i + (l & 31);
+      qa[i][0] = s.a[piece_slot(ra, 2 * h)];
+      qa[i][1] = s.a[piece_slot(ra, 2 * h + 1)];
+      qb[i][0] = s.b[piece_slot(rb, 2 * h)];
+      qb[i][1] = s.b[piece_slot(rb, 2 * h + 1)];
+      wsa[i] = s.sa[h][ra];
+      wsb[i] = s.sb[h][rb];
     }
   };
-  auto step = [&](int buf) {
-    h2 sca[2][4], scb[2][4];
+  read_step(st[0]);
+  for (int64_t s = 0; s < nsteps; ++s) {
+    issue(s + 3);
+    h2 sca[4][4], scb[4][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      nv_scales(fa[buf][i].s, sca[i]);
-      nv_scales(fb[buf][i].s, scb[i]);
+    for (int i = 0; i < 4; ++i) {
+      nv_scales(wsa[i], sca[i]);
+      nv_scales(wsb[i], scb[i]);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int c = 0; c < 8; ++c) {  // 16-value chunk c: word c of the lane's 8, block c / 2
+      v8h fa[4], fb[4];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        acc[i][j] = nv_mfma<0>(fa[buf][i], sca[i], fb[buf][j], scb[j], acc[i][j]);
-        acc[i][j] = nv_mfma<1>(fa[buf][i], sca[i], fb[buf][j], scb[j], acc[i][j]);
-        acc[i][j] = nv_mfma<2>(fa[buf][i], sca[i], fb[buf][j], scb[j], acc[i][j]);
-        acc[i][j] = nv_mfma<3>(fa[buf][i], sca[i], fb[buf][j], scb[j], acc[i][j]);
-        acc[i][j] = nv_mfma<4>(fa[buf][i], sca[i], fb[buf][j], scb[j], acc[i][j]);
-        acc[i][j] = nv_mfma<5>(fa[buf][i], sca[i], fb[buf][j], scb[j], acc[i][j]);
-        acc[i][j] = nv_mfma<6>(fa[buf][i], sca[i], fb[buf][j], scb[j], acc[i][j]);
-        acc[i][j] = nv_mfma<7>(fa[buf][i], sca[i], fb[buf][j], scb[j], acc[i][j]);
+      for (int i = 0; i < 4; ++i) {
+        fa[i] = nv_half8(word_of(qa[i], c), sca[i][c >> 1]);
+        fb[i] = nv_half8(word_of(qb[i], c), scb[i][c >> 1]);
       }
-  };
-  load(0, 0);
-  for (int64_t k0 = 0; k0 < K; k0 += 256) {
-    if (k0 + 128 < K) load(1, k0 + 128);
-    step(0);
-    if (k0 + 128 >= K) break;
-    if (k0 + 256 < K) load(0, k0 + 256);
-    step(1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    NV_WAIT_VM_LGKM0(24);  // this thread's loads of step s + 1 have landed; steps s + 2, s + 3 pending
+    __builtin_amdgcn_s_barrier();
+    if (s + 1 < nsteps) read_step(st[(s + 1) & (kRing - 1)]);
   }
+  NV_WAIT_VM_LGKM0(0);
+#undef NV_WAIT_VM_LGKM0
   // the two tensor scales, applied once: fl32(acc * S_tA * S_tB) with the product taken in binary64
   const double ts = (double)ats[0] * (double)bts[0];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      v16f t;
+    for (int j = 0; j < 4; ++j) {
+      v16f o;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) t[r] = (float)((double)acc[i][j][r] * ts);
-      store_tile(C, M, N, m0 + 32 * i, n0 + 32 * j, t, l, 1.0f);
+      for (int r = 0; r < 16; ++r) o[r] = (float)((double)acc[i][j][r] * ts);
+      store_tile(C, M, N, am0 + wr + 32 * i, bn0 + wc + 32 * j, o, l, 1.0f);
     }
 }
 
@@ -309,33 +413,34 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const f
   if ((a_block != NVFP4_BLOCK_1D && a_block != NVFP4_BLOCK_2D) ||
       (b_block != NVFP4_BLOCK_1D && b_block != NVFP4_BLOCK_2D))
     return NVFP4_ERR_UNSUPPORTED;
-  if (M < 0 || N < 0 || K < 0 || K % 64) return NVFP4_ERR_SHAPE;
+  if (M < 0 || N < 0 || K < 0 || K % 128) return NVFP4_ERR_SHAPE;
   if ((a_block == NVFP4_BLOCK_2D && M % 16) || (b_block == NVFP4_BLOCK_2D && N % 16)) return NVFP4_ERR_SHAPE;
   if (M == 0 || N == 0) return NVFP4_OK;
   if (!c) return NVFP4_ERR_NULL;
   if (K > 0 && (!a_codes || !a_scales || !b_codes || !b_scales || !a_tensor_scale || !b_tensor_scale))
     return NVFP4_ERR_NULL;
   if (!al16(a_codes) || !al16(b_codes) || !al4(a_scales) || !al4(b_scales) || !al4(c)) return NVFP4_ERR_ALIGN;
-  const int64_t tiles_m = (M + kTile - 1) / kTile, tiles_n = (N + kTile - 1) / kTile;
+  const int64_t tiles_m = (M + kBig - 1) / kBig, tiles_n = (N + kBig - 1) / kBig;
   if (tiles_m * tiles_n > (1ll << 24)) return NVFP4_ERR_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)(tiles_m * tiles_n));
+  const uint32_t tm = (uint32_t)tiles_m, tn = (uint32_t)tiles_n;
   if (K == 0) {
     hipMemsetAsync(c, 0, sizeof(float) * (size_t)(M * N), s);
   } else if (a_block == NVFP4_BLOCK_2D) {
     if (b_block == NVFP4_BLOCK_2D)
       hipLaunchKernelGGL((nv_gemm_kernel<true, true>), grid, dim3(kThreads), 0, s, a_codes, a_scales, a_tensor_scale,
-                         b_codes, b_scales, b_tensor_scale, M, N, K, c, (uint32_t)tiles_n);
+                         b_codes, b_scales, b_tensor_scale, M, N, K, c, tm, tn);
     else
       hipLaunchKernelGGL((nv_gemm_kernel<true, false>), grid, dim3(kThreads), 0, s, a_codes, a_scales, a_tensor_scale,
-                         b_codes, b_scales, b_tensor_scale, M, N, K, c, (uint32_t)tiles_n);
+                         b_codes, b_scales, b_tensor_scale, M, N, K, c, tm, tn);
   } else {
     if (b_block == NVFP4_BLOCK_2D)
       hipLaunchKernelGGL((nv_gemm_kernel<false, true>), grid, dim3(kThreads), 0, s, a_codes, a_scales, a_tensor_scale,
-                         b_codes, b_scales, b_tensor_scale, M, N, K, c, (uint32_t)tiles_n);
+                         b_codes, b_scales, b_tensor_scale, M, N, K, c, tm, tn);
     else
       hipLaunchKernelGGL((nv_gemm_kernel<false, false>), grid, dim3(kThreads), 0, s, a_codes, a_scales,
-                         a_tensor_scale, b_codes, b_scales, b_tensor_scale, M, N, K, c, (uint32_t)tiles_n);
+                         a_tensor_scale, b_codes, b_scales, b_tensor_scale, M, N, K, c, tm, tn);
   }
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
@@ -347,14 +452,14 @@ nvfp4_status nvfp4_mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, c
   if (!c) return NVFP4_ERR_NULL;
   if (K > 0 && (!a_codes || !a_scales || !b_codes || !b_scales)) return NVFP4_ERR_NULL;
   if (!al16(a_codes) || !al16(b_codes) || !al4(a_scales) || !al4(b_scales) || !al4(c)) return NVFP4_ERR_ALIGN;
-  const int64_t tiles_m = (M + kTile - 1) / kTile, tiles_n = (N + kTile - 1) / kTile;
-  if (tiles_m * tiles_n > (1ll << 24)) return NVFP4_ERR_SHAPE;
+  const int64_t bm = (M + kBig - 1) / kBig, bn = (N + kBig - 1) / kBig;
+  if (bm * bn > (1ll << 24)) return NVFP4_ERR_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (K == 0) {
     hipMemsetAsync(c, 0, sizeof(float) * (size_t)(M * N), s);
   } else {
-    hipLaunchKernelGGL(mx_gemm_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kThreads), 0, s, a_codes, a_scales,
-                       b_codes, b_scales, M, N, K, c, (uint32_t)tiles_n);
+    hipLaunchKernelGGL(mx_gemm_dma_kernel, dim3((unsigned)(bm * bn)), dim3(kThreads), 0, s, a_codes, a_scales,
+                       b_codes, b_scales, M, N, K, c, (uint32_t)bm, (uint32_t)bn);
   }
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }

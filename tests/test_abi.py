@@ -143,7 +143,7 @@ def test_gemm_validation():
 
     def g(M=64, N=64, K=128, ab=0, bb=0, ac=FAKE, c=FAKE):
         return L.nvfp4_gemm(P(ac) if ac else None, f, f, ab, f, f, f, bb, M, N, K, P(c) if c else None, None)
-    assert g(K=96) == nv.ERR_SHAPE
+    assert g(K=192) == nv.ERR_SHAPE
     assert g(M=8, ab=1) == nv.ERR_SHAPE
     assert g(N=24, bb=1) == nv.ERR_SHAPE
     assert g(ab=3) == nv.ERR_UNSUPPORTED

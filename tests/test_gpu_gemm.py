@@ -54,9 +54,10 @@ def rand_mx(rng, rows, K):
     return rng.integers(0, 256, (rows, K // 2), dtype=np.uint8), rng.integers(112, 140, (rows, K // 32), dtype=np.uint8)
 
 
-@pytest.mark.parametrize("M,N,K,a2d,b2d", [(256, 256, 256, False, False), (200, 136, 320, False, False),
-                                           (128, 160, 192, False, True), (96, 64, 64, True, True),
-                                           (1, 1, 64, False, False), (384, 257, 1024, False, False)])
+@pytest.mark.parametrize("M,N,K,a2d,b2d", [(256, 256, 256, False, False), (200, 136, 384, False, False),
+                                           (128, 160, 256, False, True), (96, 64, 128, True, True),
+                                           (1, 1, 128, False, False), (384, 272, 1152, False, True),
+                                           (520, 300, 640, False, False)])
 def test_nvfp4_gemm_random_operands(M, N, K, a2d, b2d):
     rng = np.random.default_rng(M * 7 + N + K)
     ac, asc = rand_nv(rng, M, K, a2d)
