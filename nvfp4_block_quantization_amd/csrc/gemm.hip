@@ -20,13 +20,10 @@
 // assignment of K values to the two lane halves gives the same sum, so each
 // half here walks its own contiguous K range and loads whole 16-byte pieces.
 //
-// Tiling (MXFP4): 256x256 workgroup tiles staged through an LDS ring, below.
-// Tiling (NVFP4): a workgroup of 4 waves owns a 128x128 tile of C, each wave a
-// 64x64 quarter (2x2 instruction tiles); operand fragments come straight from
-// global memory (each 16-byte piece feeds two instructions of the wave and the
-// neighbouring waves hit it in L2), with the next K step's fragments loaded
-// while the current step's instructions run, and are expanded to fp16 in
-// registers.
+// Tiling (both formats): a workgroup of 4 waves owns a 256x256 tile of C, each
+// wave a 128x128 quarter (4x4 instruction tiles, 256 fp32 accumulators per lane);
+// 128-value K steps are staged in a ring of four LDS stages, filled by direct
+// global-to-LDS loads three steps ahead of the step being computed.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -45,8 +42,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: s
 constexpr int kThreads = 256;
 
 // Dispatch order: consecutive workgroups go round-robin over the 8 XCDs; give
-// each XCD one contiguous range of tiles (N fastest), so the tiles that share
-// A rows run on the same XCD and meet in its L2.
+// each XCD one contiguous range of tile numbers (grouped_tile below turns them
+// into tiles), so the tiles that share operands run on the same XCD and meet in
+// its L2.
 __device__ __forceinline__ uint32_t xcd_tile(uint32_t bid, uint32_t nb) {
   const uint32_t q = nb >> 3, rem = nb & 7;
   const uint32_t xcd = bid & 7, slot = bid >> 3;
@@ -54,7 +52,7 @@ __device__ __forceinline__ uint32_t xcd_tile(uint32_t bid, uint32_t nb) {
 }
 
 __device__ __forceinline__ void store_tile(float* __restrict__ C, int64_t M, int64_t N, int64_t r0, int64_t c0,
-                                           const v16f& acc, int l, float scale_unused) {
+                                           const v16f& acc, int l) {
   const int64_t col = c0 + (l & 31);
   if (col >= N) return;
 #pragma unroll
@@ -66,12 +64,10 @@ __device__ __forceinline__ void store_tile(float* __restrict__ C, int64_t M, int
 
 // ------------------------------------------------------------------ MXFP4 ---
 
-// MXFP4: a workgroup of 4 waves owns a 256x256 tile of C, each wave a 128x128
-// quarter (4x4 instruction tiles, 256 fp32 accumulators per lane).  Per
-// 128-value K step the workgroup's 256 A rows and 256 B rows (64 bytes each)
-// and their scale words are staged in LDS; every 16-byte operand piece read
-// from LDS feeds four instructions.  LDS pieces are XOR-swizzled by row so that
-// the 16 lanes of a read phase hit distinct banks.
+// Per 128-value K step the workgroup's 256 A rows and 256 B rows (64 bytes
+// each) and their scale words are staged in LDS; every 16-byte operand piece
+// read from LDS feeds four instructions.  LDS pieces are XOR-swizzled by row so
+// that the 16 lanes of a read phase hit distinct banks.
 constexpr int kBig = 256;  // workgroup tile (M and N)
 constexpr int kStepK = 128;
 
@@ -231,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_dma_kernel(const uint8_t* __
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) store_tile(C, M, N, am0 + wr + 32 * i, bn0 + wc + 32 * j, acc[i][j], l, 1.0f);
+    for (int j = 0; j < 4; ++j) store_tile(C, M, N, am0 + wr + 32 * i, bn0 + wc + 32 * j, acc[i][j], l);
 }
 #undef MX_WAIT_VM_LGKM0
 
@@ -393,7 +389,7 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(const uint8_t* __rest
       v16f o;
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[r] = (float)((double)acc[i][j][r] * ts);
-      store_tile(C, M, N, am0 + wr + 32 * i, bn0 + wc + 32 * j, o, l, 1.0f);
+      store_tile(C, M, N, am0 + wr + 32 * i, bn0 + wc + 32 * j, o, l);
     }
 }
 

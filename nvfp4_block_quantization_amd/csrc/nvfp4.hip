@@ -17,6 +17,10 @@
 //   MXFP4                       the row and strip kernels instantiated for
 //                               32-element blocks with E8M0 scales (no tensor
 //                               scale), and mx_dequant.
+//   err_stats                   round-to-nearest quantization binned by scaled
+//                               value: counts and squared errors, with an
+//                               exact-scale reference.
+// The FP4 GEMMs that consume the quantized copies are in gemm.hip.
 #include "nvfp4_device.hpp"
 
 #include <hip/hip_runtime.h>
