@@ -99,7 +99,6 @@ __device__ __forceinline__ v16f mx_mfma_s(u32x4 a, u32x4 b, uint32_t sa, uint32_
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, vb, acc, 4, 4, 2 * C, (int)sa, 2 * C, (int)sb);
 }
 
-// One 64-value chunk (c = 0, 1) of a K step: 4 A and 4 B pieces from LDS, 16 instructions.
 // Operand pieces of one 64-value chunk (CH = 0, 1) of a K step, from LDS.
 template <int CH>
 __device__ __forceinline__ void mx_read(const MxStage& s, int wr, int wc, int l, int h, u32x4 (&fa)[4],

@@ -13,10 +13,10 @@
 //                               64x64 sub-tile (and its random words) staged in
 //                               LDS and read back by columns; the column copy
 //                               leaves as whole 128-byte lines.
-//   dequant                     codes + scales + S_t -> fp32.
+//   dequant_rows                codes + scales (+ S_t) -> fp32, row by row.
 //   MXFP4                       the row and strip kernels instantiated for
 //                               32-element blocks with E8M0 scales (no tensor
-//                               scale), and mx_dequant.
+//                               scale); dequant_rows reads their E8M0 scales.
 //   err_stats                   round-to-nearest quantization binned by scaled
 //                               value: counts and squared errors, with an
 //                               exact-scale reference.
@@ -606,64 +606,39 @@ __global__ void zero_f64_kernel(double* __restrict__ p, int n) {
 
 // ------------------------------------------------------------ dequantize ---
 
-template <bool TWO_D>
-__global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __restrict__ codes,
-                                                           const uint8_t* __restrict__ scales,
-                                                           const float* __restrict__ tsp, int64_t nblocks,
-                                                           int64_t cols, float* __restrict__ out) {
-  const float st = tsp[0];
-  const int64_t nth = (int64_t)gridDim.x * kThreads;
-  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += nth) {
-    const uint2 c = *reinterpret_cast<const uint2*>(codes + 8 * b);
-    uint32_t sb;
-    if constexpr (TWO_D) {
-      const int64_t e0 = 16 * b, r = e0 / cols, c0 = e0 - r * cols;
-      sb = scales[(r / 16) * (cols / 16) + c0 / 16];
-    } else {
-      sb = scales[b];
+// Dequantize, row by row: each workgroup takes whole rows; per row, lane g
+// turns 4 codes (2 bytes) into one 16-byte float4, so every wave store
+// instruction writes 1 KB of contiguous output.
+enum DequantFormat : int { kDqNv1D = 0, kDqNv2D = 1, kDqMx = 2 };
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void dequant_rows_kernel(const uint8_t* __restrict__ codes,
+                                                                const uint8_t* __restrict__ scales,
+                                                                const float* __restrict__ tsp, int64_t rows,
+                                                                int64_t cols, float* __restrict__ out) {
+  constexpr int BLK = FMT == kDqMx ? 32 : 16;  // elements per scale
+  const float st = FMT == kDqMx ? 1.0f : tsp[0];
+  const int64_t g4 = cols / 4;
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const uint16_t* crow = reinterpret_cast<const uint16_t*>(codes + r * (cols / 2));
+    const uint8_t* srow = scales + (FMT == kDqNv2D ? r / 16 : r) * (cols / BLK);
+    float4* orow = reinterpret_cast<float4*>(out + r * cols);
+#pragma unroll 4
+    for (int64_t g = threadIdx.x; g < g4; g += kThreads) {
+      const uint32_t c4 = crow[g];
+      const uint32_t sb = srow[(4 * g) / BLK];
+      float d;
+      if constexpr (FMT == kDqMx) {  // 2^(sb - 127); E8M0 code 255 is NaN
+        d = sb == 0u ? __uint_as_float(0x00400000u) : (sb == 255u ? __uint_as_float(0x7FC00000u) : __uint_as_float(sb << 23));
+      } else {
+        d = e4m3_decode(sb) * st;
+      }
+      const f32x2 v0 = fp4_pair_values<0>(c4), v1 = fp4_pair_values<1>(c4);
+      orow[g] = make_float4(v0.x * d, v0.y * d, v1.x * d, v1.y * d);
     }
-    const float d = e4m3_decode(sb) * st;
-    f32x2 v[8];
-    v[0] = fp4_pair_values<0>(c.x);
-    v[1] = fp4_pair_values<1>(c.x);
-    v[2] = fp4_pair_values<2>(c.x);
-    v[3] = fp4_pair_values<3>(c.x);
-    v[4] = fp4_pair_values<0>(c.y);
-    v[5] = fp4_pair_values<1>(c.y);
-    v[6] = fp4_pair_values<2>(c.y);
-    v[7] = fp4_pair_values<3>(c.y);
-    float4* o = reinterpret_cast<float4*>(out + 16 * b);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      o[j] = make_float4(v[2 * j].x * d, v[2 * j].y * d, v[2 * j + 1].x * d, v[2 * j + 1].y * d);
   }
 }
 
-// MXFP4: out = value(code) * 2^(sc - 127); E8M0 code 255 is NaN.
-__global__ __launch_bounds__(kThreads) void mx_dequant_kernel(const uint8_t* __restrict__ codes,
-                                                              const uint8_t* __restrict__ scales, int64_t nblocks,
-                                                              float* __restrict__ out) {
-  const int64_t nth = (int64_t)gridDim.x * kThreads;
-  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += nth) {
-    const uint2 c = *reinterpret_cast<const uint2*>(codes + 8 * b);
-    const uint32_t sc = scales[b >> 1];  // 16 elements: half of a 32-element block
-    const float d = sc == 0u ? __uint_as_float(0x00400000u)
-                             : (sc == 255u ? __uint_as_float(0x7FC00000u) : __uint_as_float(sc << 23));
-    f32x2 v[8];
-    v[0] = fp4_pair_values<0>(c.x);
-    v[1] = fp4_pair_values<1>(c.x);
-    v[2] = fp4_pair_values<2>(c.x);
-    v[3] = fp4_pair_values<3>(c.x);
-    v[4] = fp4_pair_values<0>(c.y);
-    v[5] = fp4_pair_values<1>(c.y);
-    v[6] = fp4_pair_values<2>(c.y);
-    v[7] = fp4_pair_values<3>(c.y);
-    float4* o = reinterpret_cast<float4*>(out + 16 * b);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      o[j] = make_float4(v[2 * j].x * d, v[2 * j].y * d, v[2 * j + 1].x * d, v[2 * j + 1].y * d);
-  }
-}
 
 // ------------------------------------------------------------- dispatch ---
 
@@ -688,6 +663,7 @@ static void with_rule(int rule, F&& f) {
 }
 
 constexpr int kRowU = 1;
+constexpr int64_t kDequantMaxGrid = 4096;  // workgroups of the row-wise dequantize (grid-stride over rows)
 constexpr int kAmaxMaxParts = 1024;
 
 // Resident workgroups of a kernel on the current device (persistent grids).
@@ -878,13 +854,13 @@ nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const
   if (!codes || !scales || !tensor_scale || !out) return NVFP4_ERR_NULL;
   if (!aligned16(codes) || !aligned16(out)) return NVFP4_ERR_ALIGN;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int64_t nblocks = n / 16;
-  int64_t grid = (nblocks + kThreads - 1) / kThreads;
-  if (grid > 65536) grid = 65536;
-  with_bool(block == NVFP4_BLOCK_2D, [&](auto TWO_D) {
-    hipLaunchKernelGGL((dequant_kernel<TWO_D()>), dim3((unsigned)grid), dim3(kThreads), 0, s, codes, scales,
-                       tensor_scale, nblocks, cols, out);
-  });
+  const unsigned grid = (unsigned)(rows < kDequantMaxGrid ? rows : kDequantMaxGrid);
+  if (block == NVFP4_BLOCK_2D)
+    hipLaunchKernelGGL(dequant_rows_kernel<kDqNv2D>, dim3(grid), dim3(kThreads), 0, s, codes, scales, tensor_scale,
+                       rows, cols, out);
+  else
+    hipLaunchKernelGGL(dequant_rows_kernel<kDqNv1D>, dim3(grid), dim3(kThreads), 0, s, codes, scales, tensor_scale,
+                       rows, cols, out);
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
@@ -951,10 +927,9 @@ nvfp4_status nvfp4_mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
   if (!codes || !scales || !out) return NVFP4_ERR_NULL;
   if (!aligned16(codes) || !aligned16(out)) return NVFP4_ERR_ALIGN;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int64_t nblocks = n / 16;
-  int64_t grid = (nblocks + kThreads - 1) / kThreads;
-  if (grid > 65536) grid = 65536;
-  hipLaunchKernelGGL(mx_dequant_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, codes, scales, nblocks, out);
+  const unsigned grid = (unsigned)(rows < kDequantMaxGrid ? rows : kDequantMaxGrid);
+  hipLaunchKernelGGL(dequant_rows_kernel<kDqMx>, dim3(grid), dim3(kThreads), 0, s, codes, scales, nullptr, rows,
+                     cols, out);
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
