@@ -214,6 +214,12 @@ static float pairwise_sum(const float* t, int n) {
  *   den = fl(T * s_t); r = fl(m_b / den) (0 if m_b or den is 0)
  *   sb  = E4M3(r);     d = fl(dec(sb) * s_t); e = fl(1 / d) (0 if d is 0 or 1/d overflows)
  *   z_i = fl(y_i * e); code_i = round(z_i)
+ * Stochastic rounding draws element i's decision from its random word w_i:
+ * the scale-to-6 candidate (and plain NVFP4) uses bits 31..10 of w_i, the
+ * scale-to-4 candidate bits 30..9 (the word shifted left by one).  Both are
+ * uniform 22-bit numbers, so each candidate's rounding is unbiased; the pages
+ * fix only that the decision is random with the fractional distance as its
+ * probability, not which bits of the element's word feed it.
  * With rule != NONE, the error against the values being quantized
  * ([P2] "Adaptive block scaling", step 2) is
  *   xh_i = fl(value(code_i) * d); eps_i = fl(y_i - xh_i)
@@ -231,7 +237,8 @@ static void candidate(const float* y, int n, float m_b, float T, float s_t, int 
   }
   for (int i = 0; i < n; ++i) {
     float z = y[i] * e;
-    codes[i] = sr ? orc_e2m1_sr(z, rwords[i]) : orc_e2m1_rne(z);
+    if (!sr) codes[i] = orc_e2m1_rne(z);
+    else codes[i] = orc_e2m1_sr(z, T == 4.0f ? rwords[i] << 1 : rwords[i]);
   }
   *sb_out = sb;
   *err = 0.0f;

@@ -94,7 +94,9 @@ void orc_rht16(const float* x, uint32_t mask, float* y);
 
 /* ---- block level (exposed for the pins) -------------------------------- */
 /* Quantize one block of n (16 or 256) values y with tensor scale s_t.
- * rwords: one random word per element (used only when sr != 0; may be NULL otherwise).
+ * rwords: one random word per element (used only when sr != 0; may be NULL otherwise);
+ * the scale-to-6 candidate rounds with the word itself, the scale-to-4 candidate
+ * with the word shifted left by one (bits 30..9 become the 22-bit threshold).
  * Outputs: codes[n], *scale (E4M3 code), *chose4 (1 if the scale-to-4 candidate won),
  * err[0] = error of the scale-to-6 candidate, err[1] = scale-to-4 (0 when rule == NONE). */
 void orc_quantize_block(const float* y, int n, float s_t, int rule, int sr, const uint32_t* rwords,

@@ -311,3 +311,46 @@ def test_tie_keeps_scale_six(orc):
     for rule in RULES:
         codes, sb, ch, (e6, e4) = orc.quantize_block(y, s448, rule)
         assert sb == 0x7E and e6 == e4 and not ch
+
+
+# ------------------------------------------ stochastic rounding under 4/6
+
+@pytest.mark.parametrize("rule", RULES)
+def test_sr_candidates_use_their_own_bits(orc, wl, rule):
+    """With stochastic rounding and a 4/6 rule, each candidate's codes are the
+    stochastic roundings of its own scaled values: scale-to-6 with the element's
+    word, scale-to-4 with the word shifted left by one.  The candidate's scaled
+    values are recomputed here from the E4M3 scale the oracle picked (binary32
+    steps in the same order), then rounded by the pinned e2m1_sr."""
+    x = _bf16_to_f32(wl.generate(5, 32, 256, seed=21))
+    s_t = np.float32(orc.tensor_scale(orc.amax(x), 256.0))
+    blocks = x.reshape(-1, 16)
+    idx = np.arange(blocks.size, dtype=np.uint64).reshape(-1, 16)
+    seen = {0: 0, 1: 0}
+    for b, blk in enumerate(blocks):
+        w = orc.sr_words(77, idx[b])
+        codes, sb, ch, _ = orc.quantize_block(blk, s_t, rule, True, w)
+        d = np.float32(np.float32(orc.e4m3_value(int(sb))) * s_t)
+        e = np.float32(np.float32(1.0) / d)
+        z = (blk * e).astype(np.float32)
+        words = (w.astype(np.uint64) << 1).astype(np.uint32) if ch else w
+        assert np.array_equal(codes, orc.e2m1_sr(z, words)), (b, ch)
+        seen[int(ch)] += 1
+    assert seen[0] > 0 and seen[1] > 0  # both candidates won somewhere
+
+
+def test_sr_shifted_word_is_unbiased(orc):
+    """The scale-to-4 candidate's threshold (bits 30..9 of the Philox word) is
+    uniform too: stochastic rounding with the shifted words is unbiased to within
+    sampling noise at every fractional position."""
+    n = 1 << 18
+    w = orc.sr_words(31, np.arange(n, dtype=np.uint64))
+    ws = (w.astype(np.uint64) << 1).astype(np.uint32)
+    vals = np.array([orc.e2m1_value(int(c)) for c in range(16)])
+    for a in (0.1, 0.3, 0.75, 1.2, 1.9, 2.5, 3.3, 4.6, 5.9):
+        z = np.full(n, a, np.float32)
+        mean = vals[orc.e2m1_sr(z, ws)].mean()
+        lo = GRID[GRID <= a].max()
+        hi = GRID[GRID > a].min()
+        sd = (hi - lo) * 0.5 / np.sqrt(n)
+        assert abs(mean - np.float32(a)) < 6 * sd, (a, mean)
