@@ -325,13 +325,17 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
                                                                uint32_t strips_x, QuantParams p) {
   constexpr bool TWO_D = FMT == kFmt2D;
   constexpr bool MX = FMT == kFmtMX;
-  constexpr int VP = 68;  // LDS pitch (dwords) of the staged sub-tile: 64 values + 16 bytes of padding
+  // The staged sub-tile keeps the input's own width: bf16 inputs are staged as
+  // bf16 (a 9 KB array instead of 17 KB, so four workgroups fit in a CU's LDS)
+  // and widened again when read; binary32 inputs are staged as binary32.
+  constexpr bool HALF = DT == kBF16;
+  constexpr int VP = HALF ? 36 : 68;  // LDS pitch (dwords) of the staged sub-tile: 64 values + 16 bytes of padding
   constexpr int WP = SR ? 68 : 1;
   constexpr int CP = 36;  // LDS pitch (dwords) of the column-copy codes: 128 bytes + 16 of padding
   // column-copy scale bytes per column of the strip: 16 (NVFP4 1D), 8 (MXFP4); 2D: 16 per tile column
   constexpr int SPC = MX ? 8 : 16;
   __shared__ f32x2 tab[128];
-  __shared__ float lds_v[64 * VP];
+  __shared__ uint32_t lds_v[64 * VP];
   __shared__ uint32_t lds_w[SR ? 64 * WP : 1];
   __shared__ uint32_t col_codes[64 * CP];
   __shared__ uint32_t col_scales[TWO_D ? 16 : 64 * SPC / 4];
@@ -401,12 +405,18 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
     }
     if (!p.emit_col) return;  // uniform across the workgroup
 
-    // ---- stage the sub-tile (and its random words) in LDS as binary32
+    // ---- stage the sub-tile (and its random words) in LDS
     {
       const int row = 16 * bi + i;
-      float4* dv = reinterpret_cast<float4*>(lds_v + row * VP + 16 * bj);
+      if constexpr (HALF) {
+        uint4* dv = reinterpret_cast<uint4*>(lds_v + row * VP + 8 * bj);
+        dv[0] = raw.v[0];
+        dv[1] = raw.v[1];
+      } else {
+        float4* dv = reinterpret_cast<float4*>(lds_v + row * VP + 16 * bj);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dv[j] = make_float4(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]);
+        for (int j = 0; j < 4; ++j) dv[j] = make_float4(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]);
+      }
       if constexpr (SR) {
         uint4* dw = reinterpret_cast<uint4*>(lds_w + row * WP + 16 * bj);
 #pragma unroll
@@ -420,7 +430,11 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const int row = 16 * bi + k;
-      y[k] = lds_v[row * VP + col];
+      if constexpr (HALF) {
+        y[k] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(lds_v)[row * 2 * VP + col] << 16);
+      } else {
+        y[k] = __uint_as_float(lds_v[row * VP + col]);
+      }
       if constexpr (SR) w[k] = lds_w[row * WP + col];
     }
     float mcol = 0.0f;
@@ -437,11 +451,15 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
       cc = mx_round16<SR>(y, sbc, w);
     } else if constexpr (TWO_D) {
       // same values, same reciprocal, same words: the codes of the row copy, transposed
-      if constexpr (SR) {
+      if constexpr (SR && RULE != kRuleNone) {
+        cc = round16_sr_chosen(y, res.e, w, res.four);
+      } else {
+        if constexpr (SR) {
 #pragma unroll
-        for (int k = 1; k < 16; k += 2) w[k] >>= 1;
+          for (int k = 1; k < 16; k += 2) w[k] >>= 1;
+        }
+        cc = round16<SR>(y, res.e, w);
       }
-      cc = round16<SR>(y, res.e, w);
       sbc = res.sb;
     } else {
       const BlockResult rc = quant_block16<SR, RULE>(y, w, tab, ts.den6, ts.den4);

@@ -259,6 +259,64 @@ __device__ __forceinline__ BlockCodes round16(const float* y, float e, const uin
   return c;
 }
 
+// Stochastic rounding of 16 values under both 4/6 candidates, one convert per
+// element: the convert's first slot rounds z6 = y * e6 with bits 31..10 of the
+// element's word and its second slot z4 = y * e4 with bits 30..9 (it reads the
+// same word one bit lower), which is the bit split the two candidates use.
+// Element k lands in byte (k & 7) >> 1 of register P[2 (k >> 3) + (k & 1)], so
+// that one shift and one bitfield insert per 8 elements gather either
+// candidate's nibbles in element order.
+template <int SEL>
+__device__ __forceinline__ uint32_t sr_pair_byte(uint32_t d, const float* y, int k, float e6, float e4,
+                                                 const uint32_t* w) {
+  return cvt_sr_byte<SEL>(d, f32x2{y[k] * e6, y[k] * e4}, w[k]);
+}
+
+__device__ __forceinline__ void sr_pair_regs(const float* y, float e6, float e4, const uint32_t* w, uint32_t* P) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int k0 = (r >> 1) * 8 + (r & 1);  // elements k0, k0 + 2, k0 + 4, k0 + 6
+    uint32_t d = cvt_sr_byte0_fresh(f32x2{y[k0] * e6, y[k0] * e4}, w[k0]);
+    d = sr_pair_byte<1>(d, y, k0 + 2, e6, e4, w);
+    d = sr_pair_byte<2>(d, y, k0 + 4, e6, e4, w);
+    d = sr_pair_byte<3>(d, y, k0 + 6, e6, e4, w);
+    P[r] = d;
+  }
+}
+
+// (a & 0x0F0F0F0F) | (b & 0xF0F0F0F0): one v_bfi_b32.
+__device__ __forceinline__ uint32_t nibble_merge(uint32_t a, uint32_t b) {
+  return (a & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+}
+
+struct CodePair {
+  BlockCodes c6, c4;
+};
+
+__device__ __forceinline__ CodePair round16_sr_both(const float* y, float e6, float e4, const uint32_t* w) {
+  uint32_t P[4];
+  sr_pair_regs(y, e6, e4, w, P);
+  CodePair cp;
+  cp.c6.lo = nibble_merge(P[0], P[1] << 4);
+  cp.c6.hi = nibble_merge(P[2], P[3] << 4);
+  cp.c4.lo = nibble_merge(P[0] >> 4, P[1]);
+  cp.c4.hi = nibble_merge(P[2] >> 4, P[3]);
+  return cp;
+}
+
+// The codes of the candidate already chosen (four = 1: scale to 4), rounded
+// with that candidate's bits of each word: both slots get the same scaled value
+// and the chosen slot's nibbles are kept.
+__device__ __forceinline__ BlockCodes round16_sr_chosen(const float* y, float e, const uint32_t* w, uint32_t four) {
+  uint32_t P[4];
+  sr_pair_regs(y, e, e, w, P);
+  const uint32_t s0 = four << 2, s1 = 4u - s0;
+  BlockCodes c;
+  c.lo = nibble_merge(P[0] >> s0, P[1] << s1);
+  c.hi = nibble_merge(P[2] >> s0, P[3] << s1);
+  return c;
+}
+
 // Per-element error terms of one candidate: t_i = eps_i^2 (MSE) or |eps_i|
 // (MAE, MAXERR) with eps_i = fl(y_i - fl(value_i * d)).
 template <int RULE>
@@ -369,6 +427,52 @@ struct BlockResult {
   uint32_t four = 0;  // 1 when the scale-to-4 candidate was chosen
 };
 
+// Both candidates of a block (or of a 16x16 tile spread over a DPP row, TILE)
+// whose max is m, and the 4/6 choice.  Without 4/6 only the scale-to-6
+// candidate is formed; its stochastic rounding pairs consecutive elements in
+// one convert, so the odd elements' words are shifted right by one (the
+// convert's second slot reads its word one bit lower).
+template <bool SR, int RULE, bool TILE = false>
+__device__ __forceinline__ BlockResult choose16(const float* y, float m, const uint32_t* w, const f32x2* tab,
+                                                const Divisor& den6, const Divisor& den4) {
+  const Scale s6 = block_scale(m, den6, tab);
+  if constexpr (RULE == kRuleNone) {
+    uint32_t ws[16];
+    if constexpr (SR) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) ws[k] = (k & 1) ? (w[k] >> 1) : w[k];
+    }
+    return BlockResult{round16<SR>(y, s6.e, ws), s6.sb, s6.e};
+  } else {
+    const Scale s4 = block_scale(m, den4, tab);
+    BlockCodes c6, c4;
+    if constexpr (SR) {
+      const CodePair cp = round16_sr_both(y, s6.e, s4.e, w);
+      c6 = cp.c6;
+      c4 = cp.c4;
+    } else {
+      c6 = round16<false>(y, s6.e, nullptr);
+      c4 = round16<false>(y, s4.e, nullptr);
+    }
+    float t[16];
+    error_terms16<RULE>(y, c6, s6.d, t);
+    float err6 = reduce16<RULE>(t);
+    error_terms16<RULE>(y, c4, s4.d, t);
+    float err4 = reduce16<RULE>(t);
+    if constexpr (TILE) {
+      if constexpr (RULE == kRuleMaxErr) {
+        err6 = row16_max(err6);
+        err4 = row16_max(err4);
+      } else {
+        err6 = row16_pairwise_sum(err6);
+        err4 = row16_pairwise_sum(err4);
+      }
+    }
+    const bool pick4 = err4 < err6;  // a tie keeps the scale-to-6 block
+    return pick4 ? BlockResult{c4, s4.sb, s4.e, 1u} : BlockResult{c6, s6.sb, s6.e, 0u};
+  }
+}
+
 // One 16-element block held by one lane.  den6: fl(6 * S_t), den4: fl(4 * S_t).
 template <bool SR, int RULE>
 __device__ __forceinline__ BlockResult quant_block16(const float* y, const uint32_t* w, const f32x2* tab,
@@ -376,26 +480,7 @@ __device__ __forceinline__ BlockResult quant_block16(const float* y, const uint3
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(y[i]));
-  uint32_t ws[16];
-  if constexpr (SR) {
-#pragma unroll
-    for (int k = 0; k < 16; ++k) ws[k] = (k & 1) ? (w[k] >> 1) : w[k];
-  }
-  const Scale s6 = block_scale(m, den6, tab);
-  const BlockCodes c6 = round16<SR>(y, s6.e, ws);
-  if constexpr (RULE == kRuleNone) {
-    return BlockResult{c6, s6.sb, s6.e};
-  } else {
-    const Scale s4 = block_scale(m, den4, tab);
-    const BlockCodes c4 = round16<SR>(y, s4.e, ws);
-    float t[16];
-    error_terms16<RULE>(y, c6, s6.d, t);
-    const float err6 = reduce16<RULE>(t);
-    error_terms16<RULE>(y, c4, s4.d, t);
-    const float err4 = reduce16<RULE>(t);
-    const bool pick4 = err4 < err6;  // a tie keeps the scale-to-6 block
-    return pick4 ? BlockResult{c4, s4.sb, s4.e, 1u} : BlockResult{c6, s6.sb, s6.e, 0u};
-  }
+  return choose16<SR, RULE>(y, m, w, tab, den6, den4);
 }
 
 // A 16x16 tile spread over the 16 lanes of a DPP row, one tile row per lane.
@@ -409,33 +494,7 @@ __device__ __forceinline__ BlockResult quant_tile_row16(const float* y, const ui
 #pragma unroll
   for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(y[i]));
   m = row16_max(m);
-  uint32_t ws[16];
-  if constexpr (SR) {
-#pragma unroll
-    for (int k = 0; k < 16; ++k) ws[k] = (k & 1) ? (w[k] >> 1) : w[k];
-  }
-  const Scale s6 = block_scale(m, den6, tab);
-  const BlockCodes c6 = round16<SR>(y, s6.e, ws);
-  if constexpr (RULE == kRuleNone) {
-    return BlockResult{c6, s6.sb, s6.e};
-  } else {
-    const Scale s4 = block_scale(m, den4, tab);
-    const BlockCodes c4 = round16<SR>(y, s4.e, ws);
-    float t[16];
-    error_terms16<RULE>(y, c6, s6.d, t);
-    float err6 = reduce16<RULE>(t);
-    error_terms16<RULE>(y, c4, s4.d, t);
-    float err4 = reduce16<RULE>(t);
-    if constexpr (RULE == kRuleMaxErr) {
-      err6 = row16_max(err6);
-      err4 = row16_max(err4);
-    } else {
-      err6 = row16_pairwise_sum(err6);
-      err4 = row16_pairwise_sum(err4);
-    }
-    const bool pick4 = err4 < err6;
-    return pick4 ? BlockResult{c4, s4.sb, s4.e, 1u} : BlockResult{c6, s6.sb, s6.e, 0u};
-  }
+  return choose16<SR, RULE, true>(y, m, w, tab, den6, den4);
 }
 
 // ----------------------------------------------------------------- MXFP4 ---
