@@ -128,8 +128,10 @@ nvfp4_status nvfp4_amax(const void* x, nvfp4_dtype dtype, int64_t rows, int64_t 
  * Stochastic rounding: the element with index idx = (row_offset + r) * cols + c uses word
  *   (idx mod 4) of Philox-4x32-10 at key (sr_seed low, high), counter (q low, q high, 0, 0),
  *   q = idx / 4; it rounds up iff (word >> 10) + floor(f * 2^22) >= 2^22, f the fractional
- *   distance to the next grid point.  Both copies and both candidates use the same word.
- * Shapes: cols % 16 == 0; rows % 16 == 0 when a column copy or 2D tiles are requested.
+ *   distance to the next grid point.  Both copies use the element's word; with a 4/6 rule the
+ *   scale-to-4 candidate rounds with the word shifted left by one (its bits 30..9).
+ * Shapes: cols % 16 == 0; rows % 16 == 0 and cols <= 2^24 when a column copy or 2D tiles are
+ * requested.
  * Unsupported (NVFP4_ERR_UNSUPPORTED): rht with 2D or with a column copy; scale_cap other than
  * 448 or 256; no copy requested; an unknown rule or block kind.
  *   x          device, 16-byte aligned
@@ -209,8 +211,8 @@ typedef struct {
   uint8_t* scales_col;
 } nvfp4_mx_outputs;
 
-/* One pass over x, no amax needed.  Shapes: cols % 32 == 0; rows % 32 == 0 with a
- * column copy.  NVFP4_ERR_UNSUPPORTED if no copy is requested.
+/* One pass over x, no amax needed.  Shapes: cols % 32 == 0; rows % 32 == 0 and
+ * cols <= 2^24 with a column copy.  NVFP4_ERR_UNSUPPORTED if no copy is requested.
  *   x    device, 16-byte aligned;  cfg, out: host pointers */
 nvfp4_status nvfp4_mxfp4_quantize(const void* x, nvfp4_dtype dtype, int64_t rows, int64_t cols,
                                   const nvfp4_mx_config* cfg, const nvfp4_mx_outputs* out, void* stream);

@@ -306,6 +306,7 @@ __global__ __launch_bounds__(kThreads) void quant_row_kernel(const void* __restr
 // the four strips that share the row copy's 128-byte lines run back to back
 // on one XCD and meet in its L2.
 constexpr int kStripRows = 256;
+constexpr int64_t kStripMaxCols = 1ll << 24;  // column copies and 16x16 tiles: at most 2^24 columns
 
 __device__ __forceinline__ uint32_t xcd_order(uint32_t bid, uint32_t nb) {
   const uint32_t q = nb >> 3, rem = nb & 7;
@@ -351,35 +352,52 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
   const int nsub = (int)((rows_left < kStripRows ? rows_left : kStripRows) + 63) / 64;
   const bool col_ok = c0 < cols;
 
-  // Element index of this lane's first element in sub-tile q: e(q) = e(0) + q * 64 * cols.
-  // Input, output and random-stream addresses all advance by that uniform stride.
+  // Element index of this lane's first element in sub-tile q: E(q) + L, with
+  // E(q) = sr0 * cols + 64 sx + 64 q cols the same for the whole workgroup and
+  // L = (16 bi + i) cols + 16 bj the lane's offset inside the sub-tile.  Input,
+  // output and random-stream addresses are a uniform base plus a 32-bit lane
+  // offset (cols <= 2^24, checked on the host, keeps L times the element size
+  // below 2^32).
   const int64_t e_step = 64 * cols;
+  const uint32_t L = (uint32_t)(16 * bi + i) * (uint32_t)cols + 16u * (uint32_t)bj;
+  const uint32_t lmax = 63u * (uint32_t)cols + 48u;  // the largest L in the workgroup
+  constexpr uint32_t ES = DT == kBF16 ? 2u : 4u;     // input bytes per element
   auto lane_valid = [&](int q) { return col_ok && sr0 + 64 * q + 16 * bi < rows; };  // whole 16x16 blocks
   // Input of sub-tile q for this lane (lanes of blocks outside the tensor read
-  // its first elements and store nothing).
-  auto load_sub = [&](int q, int64_t e, RawBlock<DT>& raw) {
-    const int64_t e0 = lane_valid(q) ? e : 0;
-    const uint4* src = reinterpret_cast<const uint4*>(x) + (e0 >> (DT == kBF16 ? 3 : 2));
+  // the sub-tile's first elements, which exist, and store nothing).
+  auto load_sub = [&](int q, int64_t eq, RawBlock<DT>& raw) {
+    const uint32_t off = lane_valid(q) ? L * ES : 0u;
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(x) + eq * ES + off);
 #pragma unroll
     for (int j = 0; j < (DT == kBF16 ? 2 : 4); ++j) raw.v[j] = src[j];
   };
-  const int64_t e_first = (sr0 + 16 * bi + i) * cols + c0;
+  const int64_t e_first = sr0 * cols + (int64_t)sx * 64;
   RawBlock<DT> buf0, buf1;
   load_sub(0, e_first, buf0);
   TensorScale ts{};
   if constexpr (!MX) ts = workgroup_setup(p, tab);
 
-  // One 64x64 sub-tile; prefetches sub-tile q + 1 into `nxt`.
-  auto sub_tile = [&](int q, int64_t e, const RawBlock<DT>& raw, RawBlock<DT>& nxt) {
+  // One 64x64 sub-tile whose uniform element base is eq; prefetches sub-tile q + 1 into `nxt`.
+  auto sub_tile = [&](int q, int64_t eq, const RawBlock<DT>& raw, RawBlock<DT>& nxt) {
     const int64_t r0 = sr0 + 64 * q + 16 * bi;  // first row of this lane's 16x16 block
     const bool valid = lane_valid(q);
-    if (q + 1 < nsub) load_sub(q + 1, e + e_step, nxt);
+    if (q + 1 < nsub) load_sub(q + 1, eq + e_step, nxt);
 
-    // ---- row pass: lane i holds row r0 + i, columns c0 .. c0 + 15 (element index e ..)
+    // ---- row pass: lane i holds row r0 + i, columns c0 .. c0 + 15 (element index eq + L ..)
     float y[16];
     uint32_t w[16];
     unpack_raw<DT>(raw, y);
-    if constexpr (SR) sr_words16((uint64_t)(e + p.idx_base), p.k0, p.k1, w);
+    if constexpr (SR) {
+      // Philox counters (idx / 4): a uniform part and the lane's L / 4; when no
+      // lane's low counter word wraps (always, short of 2^34-element strides),
+      // the high word is uniform and the low word a 32-bit add
+      const uint64_t qu = (uint64_t)(eq + p.idx_base) >> 2;
+      if ((uint64_t)(uint32_t)qu + (lmax >> 2) + 3u < (1ull << 32)) {
+        sr_words16_hi_uniform((uint32_t)qu + (L >> 2), (uint32_t)(qu >> 32), p.k0, p.k1, w);
+      } else {
+        sr_words16((uint64_t)(eq + p.idx_base) + L, p.k0, p.k1, w);
+      }
+    }
     BlockResult res;
     if constexpr (MX) {
       // the 32-column block of columns c0 .. is shared with lane t ^ 16 (bj ^ 1)
@@ -393,14 +411,14 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
       res = quant_block16<SR, RULE>(y, w, tab, ts.den6, ts.den4);
     }
 
-    if (valid && p.emit_row) {
-      *reinterpret_cast<uint2*>(p.codes_row + (e >> 1)) = make_uint2(res.codes.lo, res.codes.hi);
+    if (valid && p.emit_row) {  // eq is a multiple of 64 (MXFP4: cols % 32 == 0, so of 32 per row too)
+      *reinterpret_cast<uint2*>(p.codes_row + (eq >> 1) + (L >> 1)) = make_uint2(res.codes.lo, res.codes.hi);
       if constexpr (MX) {
-        if ((bj & 1) == 0) p.scales_row[e >> 5] = (uint8_t)res.sb;
+        if ((bj & 1) == 0) p.scales_row[(eq >> 5) + (L >> 5)] = (uint8_t)res.sb;
       } else if constexpr (TWO_D) {
         if (i == 0) p.scales_row[(r0 / 16) * (cols / 16) + c0 / 16] = (uint8_t)res.sb;
       } else {
-        p.scales_row[e >> 4] = (uint8_t)res.sb;
+        p.scales_row[(eq >> 4) + (L >> 4)] = (uint8_t)res.sb;
       }
     }
     if (!p.emit_col) return;  // uniform across the workgroup
@@ -418,9 +436,12 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
         for (int j = 0; j < 4; ++j) dv[j] = make_float4(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]);
       }
       if constexpr (SR) {
-        uint4* dw = reinterpret_cast<uint4*>(lds_w + row * WP + 16 * bj);
+        // one 4-byte store per word: the Philox results sit in scattered
+        // registers, and 16-byte stores would first gather them with moves
+        typedef __attribute__((address_space(3))) volatile uint32_t lds_word;
+        lds_word* dw = (lds_word*)(lds_w + row * WP + 16 * bj);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dw[j] = make_uint4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
+        for (int k = 0; k < 16; ++k) dw[k] = w[k];
       }
     }
     __syncthreads();
@@ -479,11 +500,11 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
   };
 
   // Two sub-tiles per trip so that the prefetch buffers alternate without copies.
-  int64_t e = e_first;
+  int64_t eq = e_first;
   for (int q = 0; q < nsub; q += 2) {  // uniform trip count
-    sub_tile(q, e, buf0, buf1);
-    if (q + 1 < nsub) sub_tile(q + 1, e + e_step, buf1, buf0);
-    e += 2 * e_step;
+    sub_tile(q, eq, buf0, buf1);
+    if (q + 1 < nsub) sub_tile(q + 1, eq + e_step, buf1, buf0);
+    eq += 2 * e_step;
   }
   if (!p.emit_col) return;
   __syncthreads();
@@ -795,6 +816,7 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dtype, int64_t rows, int6
   if (rows < 0 || cols < 0) return NVFP4_ERR_SHAPE;
   if (cols % 16) return NVFP4_ERR_SHAPE;
   if ((two_d || ecol) && rows % 16) return NVFP4_ERR_SHAPE;
+  if ((two_d || ecol) && cols > kStripMaxCols) return NVFP4_ERR_SHAPE;
   const int64_t n = rows * cols;
   if (n > 0) {
     if (!x) return NVFP4_ERR_NULL;
@@ -890,6 +912,7 @@ nvfp4_status nvfp4_mxfp4_quantize(const void* x, nvfp4_dtype dtype, int64_t rows
   if (!erow && !ecol) return NVFP4_ERR_UNSUPPORTED;
   if (rows < 0 || cols < 0 || cols % 32) return NVFP4_ERR_SHAPE;
   if (ecol && rows % 32) return NVFP4_ERR_SHAPE;
+  if (ecol && cols > kStripMaxCols) return NVFP4_ERR_SHAPE;
   const int64_t n = rows * cols;
   if (n == 0) return NVFP4_OK;
   if (!x) return NVFP4_ERR_NULL;

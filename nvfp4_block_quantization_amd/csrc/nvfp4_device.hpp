@@ -124,6 +124,66 @@ __device__ __forceinline__ U4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c
   return U4{c0, c1, c2, c3};
 }
 
+// Philox-4x32-10 for counters (c0, c1, 0, 0) whose high word c1 is the same
+// for the whole wave: the first round's second product is zero and its xor of
+// c1 with the key is wave-uniform, so the second round's first product and the
+// third round's c3 term are uniform too and run on the scalar unit.  Same
+// results as philox4x32_10(c0, c1, 0, 0, k0, k1).
+__device__ __forceinline__ U4 philox4x32_10_hi_uniform(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1) {
+  // round 1 (c2 = c3 = 0)
+  uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+  uint32_t n0 = c1 ^ k0;                       // uniform
+  uint32_t n2 = (uint32_t)(p0 >> 32) ^ k1;
+  uint32_t x1 = 0u, x3 = (uint32_t)p0;
+  k0 += 0x9E3779B9u;
+  k1 += 0xBB67AE85u;
+  // round 2 (c0 = n0 uniform, c1 = 0)
+  uint64_t pu = (uint64_t)0xD2511F53u * n0;    // uniform
+  uint64_t p1 = (uint64_t)0xCD9E8D57u * n2;
+  uint32_t m0 = (uint32_t)(p1 >> 32) ^ k0;
+  uint32_t m2 = x3 ^ ((uint32_t)(pu >> 32) ^ k1);
+  x1 = (uint32_t)p1;
+  x3 = (uint32_t)pu;                           // uniform
+  k0 += 0x9E3779B9u;
+  k1 += 0xBB67AE85u;
+  // round 3 (c3 uniform)
+  p0 = (uint64_t)0xD2511F53u * m0;
+  p1 = (uint64_t)0xCD9E8D57u * m2;
+  uint32_t c0n = xor3((uint32_t)(p1 >> 32), x1, k0);
+  uint32_t c2n = (uint32_t)(p0 >> 32) ^ (x3 ^ k1);
+  uint32_t c1n = (uint32_t)p1, c3n = (uint32_t)p0;
+  k0 += 0x9E3779B9u;
+  k1 += 0xBB67AE85u;
+#pragma unroll
+  for (int r = 3; r < 10; ++r) {
+    const uint64_t q0 = (uint64_t)0xD2511F53u * c0n;
+    const uint64_t q1 = (uint64_t)0xCD9E8D57u * c2n;
+    const uint32_t a = xor3((uint32_t)(q1 >> 32), c1n, k0);
+    const uint32_t b = xor3((uint32_t)(q0 >> 32), c3n, k1);
+    c1n = (uint32_t)q1;
+    c3n = (uint32_t)q0;
+    c0n = a;
+    c2n = b;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return U4{c0n, c1n, c2n, c3n};
+}
+
+// Words for 16 consecutive elements whose first Philox counter is (lo, hi)
+// with lo + 3 < 2^32: counters (lo + j, hi, 0, 0), j = 0..3.
+__device__ __forceinline__ void sr_words16_hi_uniform(uint32_t lo, uint32_t hi, uint32_t k0, uint32_t k1,
+                                                      uint32_t* w) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const U4 r = philox4x32_10_hi_uniform(lo + j, hi, k0, k1);
+    w[4 * j + 0] = r.x;
+    w[4 * j + 1] = r.y;
+    w[4 * j + 2] = r.z;
+    w[4 * j + 3] = r.w;
+  }
+}
+
 // Words for 16 consecutive elements starting at idx0 (idx0 % 4 == 0):
 // element idx uses word (idx mod 4) of the block at counter (idx/4, 0, 0).
 __device__ __forceinline__ void sr_words16(uint64_t idx0, uint32_t k0, uint32_t k1, uint32_t* w) {

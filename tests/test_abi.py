@@ -50,6 +50,8 @@ def test_quantize_validation():
     assert _q(rows=-1) == nv.ERR_SHAPE
     assert _q(rows=8, cfg=nv.make_config(colwise=True)) == nv.ERR_SHAPE
     assert _q(rows=8, cfg=nv.make_config(block="2d")) == nv.ERR_SHAPE
+    assert _q(rows=16, cols=(1 << 24) + 16, cfg=nv.make_config(colwise=True)) == nv.ERR_SHAPE
+    assert _q(rows=16, cols=(1 << 24) + 16, cfg=nv.make_config(block="2d")) == nv.ERR_SHAPE
     assert _q(cfg=nv.make_config(block="2d", rht=True)) == nv.ERR_UNSUPPORTED
     assert _q(cfg=nv.make_config(colwise=True, rht=True)) == nv.ERR_UNSUPPORTED
     assert _q(cfg=nv.make_config(scale_cap=300.0)) == nv.ERR_UNSUPPORTED
@@ -100,6 +102,7 @@ def test_mxfp4_validation():
     assert _mx(cols=48) == nv.ERR_SHAPE
     assert _mx(rows=-32) == nv.ERR_SHAPE
     assert _mx(rows=48, cfg=nv.MXConfig(0, 1, 0, 0, 0)) == nv.ERR_SHAPE
+    assert _mx(rows=32, cols=(1 << 24) + 32, cfg=nv.MXConfig(0, 1, 0, 0, 0)) == nv.ERR_SHAPE
     assert _mx(cfg=nv.MXConfig(0, 0, 0, 0, 0)) == nv.ERR_UNSUPPORTED
     assert _mx(dtype=2) == nv.ERR_DTYPE
     assert _mx(x=0) == nv.ERR_NULL

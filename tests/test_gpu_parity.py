@@ -110,11 +110,16 @@ def test_option_matrix(rule, sr, dtype, path):
     compare_all(x, c, f"matrix-{path}-{dtype}-{rule}-sr{int(sr)}")
 
 
-def test_row_offset_keys_the_random_stream():
+# Row offsets: a small one; one whose Philox counters (idx / 4) have a nonzero
+# high word; one whose counters cross 2^32 inside the tensor (the low counter
+# word wraps between lanes of one workgroup).
+@pytest.mark.parametrize("row_offset", [4096, (1 << 36) // 96, (1 << 34) // 96 - 20])
+@pytest.mark.parametrize("block", ["1d", "2d"])
+def test_row_offset_keys_the_random_stream(row_offset, block):
     x = workloads.generate(5, 64, 96, seed=4)
-    c = dict(rows=64, cols=96, block="1d", emit_row=True, emit_col=True, rht=False, sr=True, sr_seed=7,
-             rule="mae", cap=256.0, row_offset=4096)
-    compare_all(x, c, "row-offset")
+    c = dict(rows=64, cols=96, block=block, emit_row=True, emit_col=True, rht=False, sr=True, sr_seed=7,
+             rule="mae", cap=256.0, row_offset=row_offset)
+    compare_all(x, c, f"row-offset-{row_offset}-{block}")
 
 
 def test_dequantize_matches_oracle():
