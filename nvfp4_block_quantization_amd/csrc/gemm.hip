@@ -392,6 +392,18 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(const uint8_t* __rest
     }
 }
 
+// C = 0 for K == 0 (a kernel rather than a memset, so that the call can sit in
+// a captured graph).
+__global__ void zero_c_kernel(float* __restrict__ c, int64_t n) {
+  for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += (int64_t)gridDim.x * blockDim.x)
+    c[k] = 0.0f;
+}
+
+__host__ void zero_c(float* c, int64_t n, hipStream_t s) {
+  const int64_t blocks = (n + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(zero_c_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(kThreads), 0, s, c, n);
+}
+
 }  // namespace fp4gemm
 
 using namespace fp4gemm;
@@ -421,7 +433,7 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const f
   const dim3 grid((unsigned)(tiles_m * tiles_n));
   const uint32_t tm = (uint32_t)tiles_m, tn = (uint32_t)tiles_n;
   if (K == 0) {
-    hipMemsetAsync(c, 0, sizeof(float) * (size_t)(M * N), s);
+    zero_c(c, M * N, s);
   } else if (a_block == NVFP4_BLOCK_2D) {
     if (b_block == NVFP4_BLOCK_2D)
       hipLaunchKernelGGL((nv_gemm_kernel<true, true>), grid, dim3(kThreads), 0, s, a_codes, a_scales, a_tensor_scale,
@@ -451,7 +463,7 @@ nvfp4_status nvfp4_mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, c
   if (bm * bn > (1ll << 24)) return NVFP4_ERR_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (K == 0) {
-    hipMemsetAsync(c, 0, sizeof(float) * (size_t)(M * N), s);
+    zero_c(c, M * N, s);
   } else {
     hipLaunchKernelGGL(mx_gemm_dma_kernel, dim3((unsigned)(bm * bn)), dim3(kThreads), 0, s, a_codes, a_scales,
                        b_codes, b_scales, M, N, K, c, (uint32_t)bm, (uint32_t)bn);

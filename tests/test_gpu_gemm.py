@@ -146,3 +146,20 @@ def test_gemm_full_size_sampled():
         assert torch.equal(c.view(torch.int32), c2.view(torch.int32))
         del c, c2
         torch.cuda.empty_cache()
+
+
+def test_gemm_empty_k_writes_zeros():
+    """K = 0: C is the empty sum, zero everywhere (written by a fill kernel)."""
+    for fmt in ("nv", "mx"):
+        M, N = 300, 72
+        out = torch.full((M, N), 7.0, device="cuda")
+        ac = torch.empty((M, 0), dtype=torch.uint8, device="cuda")
+        bc = torch.empty((N, 0), dtype=torch.uint8, device="cuda")
+        ts = torch.ones(1, device="cuda")
+        say(f"{fmt} gemm with K = 0, {M}x{N}")
+        if fmt == "nv":
+            nv.gemm(ac, ac, ts, bc, bc, ts, "1d", "1d", out=out)
+        else:
+            nv.mxfp4_gemm(ac, ac, bc, bc, out=out)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(out).item() == 0
