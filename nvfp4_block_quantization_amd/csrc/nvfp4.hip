@@ -47,6 +47,7 @@ struct QuantParams {
   uint32_t k0, k1;   // Philox key (stochastic rounding)
   int64_t row_offset;  // global row of row 0 (tile kernel)
   int64_t idx_base;    // row_offset * cols: element index of the first element (row kernel)
+  int idx_below_2_34;  // every element index of the launch is below 2^34: Philox counters have high word 0
   int emit_row, emit_col;
   uint8_t* codes_row;
   uint8_t* scales_row;
@@ -254,7 +255,14 @@ struct RowChunk {
       unpack_raw<DT>(raw[u], y);
       if constexpr (RHT) rht16(y, p.rht_mask);
       uint32_t w[16];
-      if constexpr (SR) sr_words16((uint64_t)p.idx_base + (uint64_t)(16 * b), p.k0, p.k1, w);
+      if constexpr (SR) {
+        const uint64_t idx0 = (uint64_t)p.idx_base + (uint64_t)(16 * b);
+        if (p.idx_below_2_34) {  // uniform
+          sr_words16_hi_uniform((uint32_t)(idx0 >> 2), 0u, p.k0, p.k1, w);
+        } else {
+          sr_words16(idx0, p.k0, p.k1, w);
+        }
+      }
       if constexpr (MX) {
         // a 32-element block is the 16-element halves of lanes 2k and 2k + 1
         float m = absmax16(y);
@@ -835,6 +843,7 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dtype, int64_t rows, int6
   p.k1 = (uint32_t)(cfg->sr_seed >> 32);
   p.row_offset = cfg->row_offset;
   p.idx_base = cfg->row_offset * cols;
+  p.idx_below_2_34 = p.idx_base >= 0 && p.idx_base + rows * cols <= (1ll << 34);
   p.emit_row = erow;
   p.emit_col = ecol;
   p.codes_row = out->codes_row;
@@ -927,6 +936,7 @@ nvfp4_status nvfp4_mxfp4_quantize(const void* x, nvfp4_dtype dtype, int64_t rows
   p.k1 = (uint32_t)(cfg->sr_seed >> 32);
   p.row_offset = cfg->row_offset;
   p.idx_base = cfg->row_offset * cols;
+  p.idx_below_2_34 = p.idx_base >= 0 && p.idx_base + rows * cols <= (1ll << 34);
   p.emit_row = erow;
   p.emit_col = ecol;
   p.codes_row = out->codes_row;

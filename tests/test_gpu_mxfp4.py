@@ -61,9 +61,12 @@ def test_mxfp4_row_copy_any_row_count():
     compare(x, "mx-rows50", sr=True, seed=5)
 
 
-def test_mxfp4_row_offset():
+@pytest.mark.parametrize("row_offset", [8192 * 3, (1 << 36) // 160, (1 << 34) // 160 - 20])
+@pytest.mark.parametrize("col", [True, False])
+def test_mxfp4_row_offset(row_offset, col):
+    # element indices below 2^34, above it, and crossing it inside the tensor
     x = workloads.generate(4, 64, 160, seed=2)
-    compare(x, "mx-row-offset", row=True, col=True, sr=True, seed=9, row_offset=8192 * 3)
+    compare(x, f"mx-row-offset-{row_offset}", row=True, col=col, sr=True, seed=9, row_offset=row_offset)
 
 
 def test_mxfp4_edge_cases():

@@ -114,12 +114,12 @@ def test_option_matrix(rule, sr, dtype, path):
 # high word; one whose counters cross 2^32 inside the tensor (the low counter
 # word wraps between lanes of one workgroup).
 @pytest.mark.parametrize("row_offset", [4096, (1 << 36) // 96, (1 << 34) // 96 - 20])
-@pytest.mark.parametrize("block", ["1d", "2d"])
-def test_row_offset_keys_the_random_stream(row_offset, block):
+@pytest.mark.parametrize("path", ["1d", "2d", "row"])
+def test_row_offset_keys_the_random_stream(row_offset, path):
     x = workloads.generate(5, 64, 96, seed=4)
-    c = dict(rows=64, cols=96, block=block, emit_row=True, emit_col=True, rht=False, sr=True, sr_seed=7,
-             rule="mae", cap=256.0, row_offset=row_offset)
-    compare_all(x, c, f"row-offset-{row_offset}-{block}")
+    c = dict(rows=64, cols=96, block="2d" if path == "2d" else "1d", emit_row=True, emit_col=path != "row",
+             rht=False, sr=True, sr_seed=7, rule="mae", cap=256.0, row_offset=row_offset)
+    compare_all(x, c, f"row-offset-{row_offset}-{path}")
 
 
 def test_dequantize_matches_oracle():
