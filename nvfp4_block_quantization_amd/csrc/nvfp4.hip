@@ -548,12 +548,30 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
   } else {
     constexpr int BR = MX ? 32 : 16;  // rows per column block
     const int sbytes = rows_valid / BR;
+    // a full strip's SPC scale bytes of a column are contiguous in the output:
+    // one SPC-byte store per column when that run is aligned, bytes otherwise
+    const bool whole = sbytes == SPC && ((rows / BR) % SPC) == 0 &&
+                       (reinterpret_cast<uintptr_t>(p.scales_col) % SPC) == 0;
+    if (whole) {
+      if (t < 64) {
+        const int64_t c = (int64_t)sx * 64 + t;
+        uint8_t* dst = p.scales_col + c * (rows / BR) + sr0 / BR;
+        if (c < cols) {
+          if constexpr (SPC == 16) {
+            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(cs + t * SPC);
+          } else {
+            *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(cs + t * SPC);
+          }
+        }
+      }
+    } else {
 #pragma unroll
-    for (int j = 0; j < 64 * SPC / kThreads; ++j) {
-      const int k = t + kThreads * j;  // 64 columns x SPC bytes
-      const int colk = k / SPC, b = k % SPC;
-      const int64_t c = (int64_t)sx * 64 + colk;
-      if (c < cols && b < sbytes) p.scales_col[c * (rows / BR) + sr0 / BR + b] = cs[colk * SPC + b];
+      for (int j = 0; j < 64 * SPC / kThreads; ++j) {
+        const int k = t + kThreads * j;  // 64 columns x SPC bytes
+        const int colk = k / SPC, b = k % SPC;
+        const int64_t c = (int64_t)sx * 64 + colk;
+        if (c < cols && b < sbytes) p.scales_col[c * (rows / BR) + sr0 / BR + b] = cs[colk * SPC + b];
+      }
     }
   }
 }
