@@ -340,14 +340,15 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
   constexpr bool HALF = DT == kBF16;
   constexpr int VP = HALF ? 36 : 68;  // LDS pitch (dwords) of the staged sub-tile: 64 values + 16 bytes of padding
   constexpr int WP = SR ? 68 : 1;
-  constexpr int CP = 36;  // LDS pitch (dwords) of the column-copy codes: 128 bytes + 16 of padding
+  constexpr int CP = kStripRows / 8 + 4;  // LDS pitch (dwords) of the column-copy codes: the strip's bytes + 16
+  constexpr int TR = kStripRows / 16;     // 16-row blocks (and 2D tile rows) per strip
   // column-copy scale bytes per column of the strip: 16 (NVFP4 1D), 8 (MXFP4); 2D: 16 per tile column
-  constexpr int SPC = MX ? 8 : 16;
+  constexpr int SPC = MX ? kStripRows / 32 : kStripRows / 16;
   __shared__ f32x2 tab[128];
   __shared__ uint32_t lds_v[64 * VP];
   __shared__ uint32_t lds_w[SR ? 64 * WP : 1];
   __shared__ uint32_t col_codes[64 * CP];
-  __shared__ uint32_t col_scales[TWO_D ? 16 : 64 * SPC / 4];
+  __shared__ uint32_t col_scales[TWO_D ? TR : 64 * SPC / 4];
   __shared__ float lds_m[MX ? 4 * 64 : 1];  // MXFP4: column maxima of each wave's 16 rows
 
   const uint32_t strip = xcd_order(blockIdx.x, gridDim.x);
@@ -501,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
     if constexpr (MX) {
       if ((bi & 1) == 0) csb[col * SPC + 2 * q + (bi >> 1)] = (uint8_t)sbc;
     } else if constexpr (TWO_D) {
-      if (i == 0) csb[bj * 16 + 4 * q + bi] = (uint8_t)sbc;
+      if (i == 0) csb[bj * TR + 4 * q + bi] = (uint8_t)sbc;
     } else {
       csb[col * SPC + 4 * q + bi] = (uint8_t)sbc;
     }
@@ -522,10 +523,11 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
   const int rows_valid = (int)(rows_left < kStripRows ? rows_left : kStripRows);  // a multiple of 16
   const int cbytes = rows_valid / 2;
   const bool wide = ((rows / 2) & 15) == 0;  // every column's line starts 16-byte aligned
+  constexpr int PARTS = kStripRows / 32;  // 16-byte parts of a column's codes
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < 64 * PARTS / kThreads; ++j) {
     const int k = t + kThreads * j;
-    const int colk = k >> 3, part = k & 7;
+    const int colk = k / PARTS, part = k % PARTS;
     const int64_t c = (int64_t)sx * 64 + colk;
     if (c >= cols || 16 * part >= cbytes) continue;
     uint8_t* dst = p.codes_col + c * (rows / 2) + sr0 / 2 + 16 * part;
@@ -540,10 +542,10 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
   const uint8_t* cs = reinterpret_cast<const uint8_t*>(col_scales);
   if constexpr (TWO_D) {
     const int sbytes = rows_valid / 16;  // scale bytes per tile column
-    if (t < 4 * 16) {
-      const int tc = t >> 4, j = t & 15;
+    for (int k = t; k < 4 * TR; k += kThreads) {
+      const int tc = k / TR, j = k % TR;
       const int64_t ctile = (int64_t)sx * 4 + tc;
-      if (ctile * 16 < cols && j < sbytes) p.scales_col[ctile * (rows / 16) + sr0 / 16 + j] = cs[tc * 16 + j];
+      if (ctile * 16 < cols && j < sbytes) p.scales_col[ctile * (rows / 16) + sr0 / 16 + j] = cs[tc * TR + j];
     }
   } else {
     constexpr int BR = MX ? 32 : 16;  // rows per column block
@@ -557,8 +559,10 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
         const int64_t c = (int64_t)sx * 64 + t;
         uint8_t* dst = p.scales_col + c * (rows / BR) + sr0 / BR;
         if (c < cols) {
-          if constexpr (SPC == 16) {
-            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(cs + t * SPC);
+          if constexpr (SPC >= 16) {
+#pragma unroll
+            for (int u = 0; u < SPC / 16; ++u)
+              reinterpret_cast<uint4*>(dst)[u] = reinterpret_cast<const uint4*>(cs + t * SPC)[u];
           } else {
             *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(cs + t * SPC);
           }
