@@ -344,11 +344,12 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
   constexpr int TR = kStripRows / 16;     // 16-row blocks (and 2D tile rows) per strip
   // column-copy scale bytes per column of the strip: 16 (NVFP4 1D), 8 (MXFP4); 2D: 16 per tile column
   constexpr int SPC = MX ? kStripRows / 32 : kStripRows / 16;
+  // 16-byte accesses (staging, line collection, write-out) need 16-byte alignment
   __shared__ f32x2 tab[128];
-  __shared__ uint32_t lds_v[64 * VP];
-  __shared__ uint32_t lds_w[SR ? 64 * WP : 1];
-  __shared__ uint32_t col_codes[64 * CP];
-  __shared__ uint32_t col_scales[TWO_D ? TR : 64 * SPC / 4];
+  __shared__ __attribute__((aligned(16))) uint32_t lds_v[64 * VP];
+  __shared__ __attribute__((aligned(16))) uint32_t lds_w[SR ? 64 * WP : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t col_codes[64 * CP];
+  __shared__ __attribute__((aligned(16))) uint32_t col_scales[TWO_D ? TR : 64 * SPC / 4];
   __shared__ float lds_m[MX ? 4 * 64 : 1];  // MXFP4: column maxima of each wave's 16 rows
 
   const uint32_t strip = xcd_order(blockIdx.x, gridDim.x);
