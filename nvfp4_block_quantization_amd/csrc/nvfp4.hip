@@ -339,7 +339,11 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
   // and widened again when read; binary32 inputs are staged as binary32.
   constexpr bool HALF = DT == kBF16;
   constexpr int VP = HALF ? 36 : 68;  // LDS pitch (dwords) of the staged sub-tile: 64 values + 16 bytes of padding
-  constexpr int WP = SR ? 68 : 1;
+  // LDS pitch (dwords) of the staged random words, odd: the row pass stores word
+  // k of lanes (row 16 bi + i, columns 16 bj ..) at row * WP + 16 bj + k, which
+  // an odd pitch spreads over 64 distinct banks (a pitch of 68 put four lanes
+  // on each bank); the column pass reads 64 consecutive words of a row
+  constexpr int WP = SR ? 65 : 1;
   constexpr int CP = kStripRows / 8 + 4;  // LDS pitch (dwords) of the column-copy codes: the strip's bytes + 16
   constexpr int TR = kStripRows / 16;     // 16-row blocks (and 2D tile rows) per strip
   // column-copy scale bytes per column of the strip: 16 (NVFP4 1D), 8 (MXFP4); 2D: 16 per tile column

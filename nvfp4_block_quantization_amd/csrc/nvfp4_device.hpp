@@ -73,16 +73,20 @@ __device__ __forceinline__ uint32_t cvt_sr_byte(uint32_t d, f32x2 src, uint32_t 
 }
 
 // First convert of a chain that writes all four bytes of a register: the
-// register's previous contents do not matter, so it is an output operand.
+// register's previous contents do not matter, so it is an output operand.  It
+// is an early-clobber output: the convert can write its destination byte before
+// it has read the second value, so a destination that shares a register with
+// that value makes the second slot round a value whose low byte has already
+// been replaced (seen as rare run-to-run differences in the second slot).
 __device__ __forceinline__ uint32_t cvt_sr_byte0_fresh(f32x2 src, uint32_t r) {
   uint32_t d;
-  asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0" : "=v"(d) : "v"(src), "v"(r));
+  asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0" : "=&v"(d) : "v"(src), "v"(r));
   return d;
 }
 
 __device__ __forceinline__ uint32_t cvt_rne_byte0_fresh(float a, float b) {
   uint32_t d;
-  asm("v_cvt_scalef32_pk_fp4_f32 %0, %1, %2, 1.0" : "=v"(d) : "v"(a), "v"(b));
+  asm("v_cvt_scalef32_pk_fp4_f32 %0, %1, %2, 1.0" : "=&v"(d) : "v"(a), "v"(b));
   return d;
 }
 
