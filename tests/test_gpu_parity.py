@@ -1,7 +1,8 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle, bit for
-bit, on the same seeded inputs.  Small shapes are compared whole; the five
-full-size workloads are compared on sampled row bands (the oracle recomputes
-those bands with the full tensor's amax and their global row offset)."""
+bit, on the same seeded inputs: small shapes and the five full-size workloads,
+every output byte."""
+import os
+
 import numpy as np
 import pytest
 
@@ -190,54 +191,53 @@ def test_invalid_arguments_raise_on_gpu():
         nv.quantize(xg, nv.amax(torch.zeros((8, 32), dtype=torch.bfloat16, device="cuda")))
 
 
-# ------------------------------------------------- full size, sampled ----
+# ---------------------------------------------------- full size, whole ----
 
-def _bands(rows, n=4, h=32):
-    starts = sorted({0, rows - h, (rows // 2) // 16 * 16, (rows // 3) // 16 * 16})
-    return [(s, s + h) for s in starts[:n]]
+def _oracle_threads() -> int:
+    return max(1, min(os.cpu_count() or 1, 16))
+
+
+def _assert_same(tag, key, got: np.ndarray, ref: np.ndarray) -> None:
+    if not np.array_equal(got, ref):
+        bad = np.argwhere(got != ref)
+        raise AssertionError(f"{tag}: {key} differs at {len(bad)} places, first {bad[:5].tolist()}")
 
 
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 5, "5plain"])
-def test_full_size_workloads_sampled(k):
+def test_full_size_workloads_whole(k):
+    """Every output byte of the full-size workloads against the oracle (row
+    bands of the oracle run on up to 16 host threads; blocks are independent,
+    so threading does not change its bits), then a rerun that must write the
+    same bytes."""
     c = with_mask(workloads.CONFIG5_PLAIN if k == "5plain" else workloads.CONFIGS[k])
     rows, cols = c["rows"], c["cols"]
-    say(f"full workload {k}: generating {rows}x{cols}")
+    tag = f"full workload {k}"
+    say(f"{tag}: generating {rows}x{cols}")
     x = workloads.inputs(c, seed=0)
     xg = to_gpu(x)
-    say(f"full workload {k}: GPU amax + quantize")
+    say(f"{tag}: GPU amax + quantize")
     a_t, out = gpu_quantize(xg, c)
     torch.cuda.synchronize()
-    say(f"full workload {k}: oracle amax")
+    say(f"{tag}: oracle amax")
     A = oracle.amax(x, rht=c["rht"], mask=c.get("rht_mask", 0))
     assert f32_bits(a_t.cpu().numpy())[0] == f32_bits(A)
-    st = oracle.tensor_scale(A, c["cap"])
-    assert f32_bits(out["tensor_scale"].cpu().numpy())[0] == f32_bits(st)
-    for r0, r1 in _bands(rows):
-        say(f"full workload {k}: band rows {r0}:{r1}")
-        ref = oracle.quantize(x[r0:r1], oracle_cfg(c, row_offset=r0), A)
-        if c["emit_row"]:
-            assert np.array_equal(out["codes_row"][r0:r1].cpu().numpy(), ref["codes_row"])
-            srow = out["scales_row"][r0 // 16:r1 // 16] if c["block"] == "2d" else out["scales_row"][r0:r1]
-            assert np.array_equal(srow.cpu().numpy(), ref["scales_row"])
-        if c["emit_col"]:
-            assert np.array_equal(out["codes_col"][:, r0 // 2:r1 // 2].cpu().numpy(), ref["codes_col"])
-            assert np.array_equal(out["scales_col"][:, r0 // 16:r1 // 16].cpu().numpy(), ref["scales_col"])
+    say(f"{tag}: oracle quantize on {_oracle_threads()} threads")
+    ref = oracle.quantize(x, oracle_cfg(c), A, nthreads=_oracle_threads())
+    assert f32_bits(out["tensor_scale"].cpu().numpy())[0] == f32_bits(ref["tensor_scale"])
+    for key in ("codes_row", "scales_row", "codes_col", "scales_col"):
+        if key in ref:
+            _assert_same(tag, key, out[key].cpu().numpy(), ref[key])
     # determinism: a second run writes identical bytes
-    say(f"full workload {k}: determinism rerun")
+    say(f"{tag}: determinism rerun")
     _, out2 = gpu_quantize(xg, c, a_t)
     torch.cuda.synchronize()
     for key in ("codes_row", "scales_row", "codes_col", "scales_col"):
         if key in out:
             assert torch.equal(out[key], out2[key]), key
-    # properties that hold everywhere: no NaN scale code, codes cover both signs
-    for key in ("scales_row", "scales_col"):
-        if key in out:
-            assert int(out[key].max().item()) <= 0x7E
     if k == 1:
-        say("full workload 1: dequantize")
+        say(f"{tag}: dequantize")
         d = nv.dequantize(out["codes_row"], out["scales_row"], out["tensor_scale"], rows, cols)
-        ref = oracle.quantize(x, oracle_cfg(c), A)
         r = oracle.dequantize(ref["codes_row"], ref["scales_row"], ref["tensor_scale"], rows, cols)
         assert np.array_equal(f32_bits(d.cpu().numpy()), f32_bits(r))
-    del xg, out, out2
+    del xg, out, out2, ref
     torch.cuda.empty_cache()
