@@ -6,6 +6,7 @@ leg of ``bench.py`` may import it; the product package never does.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import subprocess
@@ -48,49 +49,88 @@ class Config(ctypes.Structure):
 _lib = None
 
 
+def _signatures():
+    P = ctypes.c_void_p
+    i64, u64, u32, f32, i32 = ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_float, ctypes.c_int
+    return {
+        "orc_bf16_to_f32": (f32, [ctypes.c_uint16]),
+        "orc_e2m1_rne": (ctypes.c_uint8, [f32]),
+        "orc_e2m1_sr": (ctypes.c_uint8, [f32, u32]),
+        "orc_e2m1_value": (f32, [ctypes.c_uint8]),
+        "orc_e4m3_rne_sat": (ctypes.c_uint8, [f32]),
+        "orc_e4m3_value": (f32, [ctypes.c_uint8]),
+        "orc_philox4x32_10": (None, [P, P, P]),
+        "orc_sr_word": (u32, [u64, u64]),
+        "orc_rht_mask_from_seed": (u32, [u64]),
+        "orc_rht16": (None, [P, u32, P]),
+        "orc_quantize_block": (None, [P, i32, f32, i32, i32, P, P, P, P, P]),
+        "orc_amax": (f32, [P, i32, i64, i64, i32, u32]),
+        "orc_tensor_scale": (f32, [f32, f32]),
+        "orc_quantize": (i32, [P, i32, i64, i64, ctypes.POINTER(Config), f32, P, P, P, P, P, P, P, i32]),
+        "orc_dequantize": (None, [P, P, f32, i64, i64, i32, P]),
+        "orc_e2m1_rne_n": (None, [P, i64, P]),
+        "orc_e2m1_sr_n": (None, [P, P, i64, P]),
+        "orc_e4m3_rne_sat_n": (None, [P, i64, P]),
+        "orc_sr_words_n": (None, [u64, P, i64, P]),
+        "orc_philox_n": (None, [P, P, i64, P]),
+        "orc_e8m0_value": (f32, [ctypes.c_uint8]),
+        "orc_mx_scale_code": (ctypes.c_uint8, [f32]),
+        "orc_mxfp4_quantize": (i32, [P, i32, i64, i64, i32, i32, i32, u64, i64, P, P, P, P]),
+        "orc_mxfp4_dequantize": (None, [P, P, i64, i64, P]),
+        "orc_gemm_fp4": (i32, [i32, P, P, f32, i32, P, P, f32, i32, i64, i64, i64, P, P]),
+        "orc_error_stats": (i32, [P, i32, i64, i64, ctypes.POINTER(Config), f32, f32, i32, P]),
+    }
+
+
+def _bind(path: str) -> ctypes.CDLL:
+    L = ctypes.CDLL(path)
+    for name, (res, args) in _signatures().items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
 def lib():
     global _lib
     if _lib is None:
         src_mtime = max(os.path.getmtime(_SRC), os.path.getmtime(os.path.join(_HERE, "nvfp4_oracle.h")))
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < src_mtime:
             build()
-        L = ctypes.CDLL(_LIB)
-        P = ctypes.c_void_p
-        i64, u64, u32, f32, i32 = ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_float, ctypes.c_int
-        sig = {
-            "orc_bf16_to_f32": (f32, [ctypes.c_uint16]),
-            "orc_e2m1_rne": (ctypes.c_uint8, [f32]),
-            "orc_e2m1_sr": (ctypes.c_uint8, [f32, u32]),
-            "orc_e2m1_value": (f32, [ctypes.c_uint8]),
-            "orc_e4m3_rne_sat": (ctypes.c_uint8, [f32]),
-            "orc_e4m3_value": (f32, [ctypes.c_uint8]),
-            "orc_philox4x32_10": (None, [P, P, P]),
-            "orc_sr_word": (u32, [u64, u64]),
-            "orc_rht_mask_from_seed": (u32, [u64]),
-            "orc_rht16": (None, [P, u32, P]),
-            "orc_quantize_block": (None, [P, i32, f32, i32, i32, P, P, P, P, P]),
-            "orc_amax": (f32, [P, i32, i64, i64, i32, u32]),
-            "orc_tensor_scale": (f32, [f32, f32]),
-            "orc_quantize": (i32, [P, i32, i64, i64, ctypes.POINTER(Config), f32, P, P, P, P, P, P, P, i32]),
-            "orc_dequantize": (None, [P, P, f32, i64, i64, i32, P]),
-            "orc_e2m1_rne_n": (None, [P, i64, P]),
-            "orc_e2m1_sr_n": (None, [P, P, i64, P]),
-            "orc_e4m3_rne_sat_n": (None, [P, i64, P]),
-            "orc_sr_words_n": (None, [u64, P, i64, P]),
-            "orc_philox_n": (None, [P, P, i64, P]),
-            "orc_e8m0_value": (f32, [ctypes.c_uint8]),
-            "orc_mx_scale_code": (ctypes.c_uint8, [f32]),
-            "orc_mxfp4_quantize": (i32, [P, i32, i64, i64, i32, i32, i32, u64, i64, P, P, P, P]),
-            "orc_mxfp4_dequantize": (None, [P, P, i64, i64, P]),
-            "orc_gemm_fp4": (i32, [i32, P, P, f32, i32, P, P, f32, i32, i64, i64, i64, P, P]),
-            "orc_error_stats": (i32, [P, i32, i64, i64, ctypes.POINTER(Config), f32, f32, i32, P]),
-        }
-        for name, (res, args) in sig.items():
-            fn = getattr(L, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = L
+        _lib = _bind(_LIB)
     return _lib
+
+
+def build_variant(source: str, out_dir: str, name: str = "variant") -> str:
+    """Compile another text of nvfp4_oracle.c (same header, same flags) into
+    out_dir; the tests use this to plant a mistake in a copy of the oracle and
+    check that the pins catch it."""
+    src = os.path.join(out_dir, f"{name}.c")
+    with open(src, "w") as f:
+        f.write(source)
+    so = os.path.join(out_dir, f"lib{name}.so")
+    cmd = ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-pthread",
+           "-I", _HERE, "-o", so, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    return so
+
+
+def source() -> str:
+    with open(_SRC) as f:
+        return f.read()
+
+
+@contextlib.contextmanager
+def library(path: str):
+    """Route every call of this module through another build of the oracle
+    (e.g. one from build_variant) for the duration of the block."""
+    global _lib
+    saved = lib()
+    _lib = _bind(path)
+    try:
+        yield
+    finally:
+        _lib = saved
 
 
 def _ptr(a: np.ndarray | None):
