@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 1
+#define NVFP4_ABI_VERSION 2
 
 typedef enum {
   NVFP4_OK = 0,
@@ -72,7 +72,7 @@ typedef struct {
   int32_t emit_colwise;   /* write the column-wise copy, laid out as the transpose */
   int32_t rht;            /* 16-point random Hadamard transform on each 1x16 row block
                              before quantization ([P1] 2b); row-wise 1D only */
-  uint32_t rht_sign_mask; /* bit i set: element i of each block is negated before the transform */
+  uint16_t rht_sign_mask; /* bit i set: element i of each block is negated before the transform */
   int32_t sr;             /* 1: stochastic rounding ([P1] 2d); 0: round to nearest even */
   uint64_t sr_seed;       /* Philox-4x32-10 key for stochastic rounding */
   int64_t row_offset;     /* global row of row 0: element (r, c) has index (row_offset + r) * cols + c,
@@ -131,7 +131,8 @@ nvfp4_status nvfp4_amax(const void* x, nvfp4_dtype dtype, int64_t rows, int64_t 
  *   distance to the next grid point.  Both copies use the element's word; with a 4/6 rule the
  *   scale-to-4 candidate rounds with the word shifted left by one (its bits 30..9).
  * Shapes: cols % 16 == 0; rows % 16 == 0 and cols <= 2^24 when a column copy or 2D tiles are
- * requested.
+ * requested; rows * cols <= 2^60; row_offset >= 0 and (row_offset + rows) * cols <= 2^62
+ * (NVFP4_ERR_SHAPE otherwise).
  * Unsupported (NVFP4_ERR_UNSUPPORTED): rht with 2D or with a column copy; scale_cap other than
  * 448 or 256; no copy requested; an unknown rule or block kind.
  *   x          device, 16-byte aligned
@@ -141,7 +142,11 @@ nvfp4_status nvfp4_amax(const void* x, nvfp4_dtype dtype, int64_t rows, int64_t 
 nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dtype, int64_t rows, int64_t cols, const nvfp4_config* cfg,
                             const float* amax_dev, const nvfp4_outputs* out, void* stream);
 
-/* out[r][c] = fl(value(code) * fl(dec(sb) * S_t)), the same value the 4/6 error used.
+/* Dequantize an NVFP4 copy back to binary32.  [P1] section 1: each 16-element
+ * block (or 16x16 tile, section 2c) carries one E4M3 scale; [P2]
+ * "Implementation details": one FP32 tensor scale S_t multiplies every block
+ * scale.  So an element decodes to its E2M1 value times dec(sb) * S_t:
+ *   out[r][c] = fl(value(code) * fl(dec(sb) * S_t)), the same value the 4/6 error used.
  *   codes        device [rows][cols/2], 16-byte aligned
  *   scales       device [rows][cols/16] (block 1D) or [rows/16][cols/16] (block 2D)
  *   tensor_scale device, one float (S_t as written by nvfp4_quantize)
@@ -150,10 +155,12 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dtype, int64_t rows, int6
 nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale, int64_t rows,
                               int64_t cols, nvfp4_block block, float* out, void* stream);
 
-/* Sign mask for the Hadamard transform derived from a seed: the low 16 bits of
- * word 0 of Philox-4x32-10 at key (seed low, seed high), counter (0, 0, 0, 1)
- * (stochastic rounding only uses counters whose last word is 0). */
-uint32_t nvfp4_rht_signs_from_seed(uint64_t seed);
+/* Sign mask for the Hadamard transform derived from a seed ([P1] section 2b:
+ * the transform is randomized by a seeded sign vector; one sign per element
+ * of the 16-point block): the low 16 bits of word 0 of Philox-4x32-10 at key
+ * (seed low, seed high), counter (0, 0, 0, 1) (stochastic rounding only uses
+ * counters whose last word is 0). */
+uint16_t nvfp4_rht_signs_from_seed(uint64_t seed);
 
 /* ---- error analysis ----------------------------------------------------------
  * [P2] "Problem statement": the error of values near the block max (around the
@@ -195,7 +202,7 @@ typedef struct {
   int32_t emit_colwise;  /* 32x1 column blocks, laid out as the transpose */
   int32_t sr;            /* 1: stochastic rounding; 0: round to nearest even */
   uint64_t sr_seed;
-  int64_t row_offset;    /* as in nvfp4_config */
+  int64_t row_offset;    /* as in nvfp4_config (the same limits) */
 } nvfp4_mx_config;
 
 /* Device outputs of nvfp4_mxfp4_quantize (a copy not requested may be NULL):
@@ -236,7 +243,7 @@ nvfp4_status nvfp4_mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
  * error (measured), so |C - exact| <= 2 (K / k_i) 2^-24 sum_k |A B|, with k_i =
  * 64 values per instruction for MXFP4 and 16 for NVFP4 (plus one unit of |C|
  * for NVFP4's tensor-scale multiply).  Deterministic run to run.
- * Pointers: codes 16-byte aligned, scales and C 4-byte aligned.
+ * Pointers: codes 16-byte aligned, scales and C 4-byte aligned.  M, N, K <= 2^31.
  *
  * NVFP4: scales [M][K/16] / [N][K/16] (NVFP4_BLOCK_1D) or [M/16][K/16] /
  *   [N/16][K/16] (NVFP4_BLOCK_2D, e.g. the column copy of a 16x16-tiled weight);

@@ -26,6 +26,7 @@
 // global-to-LDS loads three steps ahead of the step being computed.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <string.h>
 
 #include <type_traits>
 
@@ -411,16 +412,24 @@ using namespace fp4gemm;
 static bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 static bool al4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
+// Each GEMM dimension at most 2^31, so that M * N and the tile counts fit in int64.
+constexpr int64_t kMaxDim = 1ll << 31;
+
 extern "C" {
 
 nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
-                        nvfp4_block a_block, const uint8_t* b_codes, const uint8_t* b_scales,
-                        const float* b_tensor_scale, nvfp4_block b_block, int64_t M, int64_t N, int64_t K, float* c,
-                        void* stream) {
+                        nvfp4_block a_block_arg, const uint8_t* b_codes, const uint8_t* b_scales,
+                        const float* b_tensor_scale, nvfp4_block b_block_arg, int64_t M, int64_t N, int64_t K,
+                        float* c, void* stream) {
+  // read from the enum's bytes: a C caller may pass any int, which validation must reject
+  int a_block, b_block;
+  memcpy(&a_block, &a_block_arg, sizeof a_block);
+  memcpy(&b_block, &b_block_arg, sizeof b_block);
   if ((a_block != NVFP4_BLOCK_1D && a_block != NVFP4_BLOCK_2D) ||
       (b_block != NVFP4_BLOCK_1D && b_block != NVFP4_BLOCK_2D))
     return NVFP4_ERR_UNSUPPORTED;
   if (M < 0 || N < 0 || K < 0 || K % 128) return NVFP4_ERR_SHAPE;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return NVFP4_ERR_SHAPE;
   if ((a_block == NVFP4_BLOCK_2D && M % 16) || (b_block == NVFP4_BLOCK_2D && N % 16)) return NVFP4_ERR_SHAPE;
   if (M == 0 || N == 0) return NVFP4_OK;
   if (!c) return NVFP4_ERR_NULL;
@@ -455,6 +464,7 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const f
 nvfp4_status nvfp4_mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                               const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, float* c, void* stream) {
   if (M < 0 || N < 0 || K < 0 || K % 128) return NVFP4_ERR_SHAPE;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return NVFP4_ERR_SHAPE;
   if (M == 0 || N == 0) return NVFP4_OK;
   if (!c) return NVFP4_ERR_NULL;
   if (K > 0 && (!a_codes || !a_scales || !b_codes || !b_scales)) return NVFP4_ERR_NULL;

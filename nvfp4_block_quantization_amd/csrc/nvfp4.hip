@@ -27,6 +27,7 @@
 #include <stdint.h>
 
 #include <math.h>
+#include <string.h>
 
 #include <type_traits>
 
@@ -759,12 +760,34 @@ using namespace nvfp4;
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The value a C caller passed for an enum-typed parameter, read from its bytes:
+// a value outside the enumerators is legal in C but may not be loaded as the
+// C++ enum type, and validation must see it to reject it.
+template <typename E>
+static int enum_bits(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized");
+  int v;
+  memcpy(&v, &e, sizeof v);
+  return v;
+}
+
+// Shapes whose element count (and byte count of a binary32 copy) fits in int64.
+constexpr int64_t kMaxElements = 1ll << 60;
+static bool dims_ok(int64_t rows, int64_t cols) {
+  return rows >= 0 && cols >= 0 && (cols == 0 || rows <= kMaxElements / cols);
+}
+
+// Element indices (row_offset + r) * cols + c of the random stream stay below 2^62.
+static bool row_offset_ok(int64_t row_offset, int64_t rows, int64_t cols) {
+  return row_offset >= 0 && (cols == 0 || row_offset <= (1ll << 62) / cols - rows);
+}
+
 extern "C" {
 
 int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
 
 const char* nvfp4_status_string(nvfp4_status s) {
-  switch (s) {
+  switch (enum_bits(s)) {
     case NVFP4_OK: return "ok";
     case NVFP4_ERR_NULL: return "a required pointer is NULL";
     case NVFP4_ERR_SHAPE: return "invalid shape (dims must be >= 0 and multiples of 16 where blocks need it)";
@@ -777,7 +800,7 @@ const char* nvfp4_status_string(nvfp4_status s) {
   return "unknown status";
 }
 
-uint32_t nvfp4_rht_signs_from_seed(uint64_t seed) {
+uint16_t nvfp4_rht_signs_from_seed(uint64_t seed) {
   // host evaluation of Philox-4x32-10 at counter (0, 0, 0, 1)
   uint32_t c0 = 0, c1 = 0, c2 = 0, c3 = 1, k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
   for (int r = 0; r < 10; ++r) {
@@ -792,7 +815,7 @@ uint32_t nvfp4_rht_signs_from_seed(uint64_t seed) {
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
-  return c0 & 0xFFFFu;
+  return (uint16_t)(c0 & 0xFFFFu);
 }
 
 static int amax_parts(int64_t rows, int64_t cols) {
@@ -804,13 +827,14 @@ static int amax_parts(int64_t rows, int64_t cols) {
 }
 
 size_t nvfp4_amax_workspace_bytes(int64_t rows, int64_t cols) {
-  if (rows < 0 || cols < 0) return 0;
+  if (!dims_ok(rows, cols)) return 0;
   return sizeof(float) * (size_t)amax_parts(rows, cols);
 }
 
-nvfp4_status nvfp4_amax(const void* x, nvfp4_dtype dtype, int64_t rows, int64_t cols, const nvfp4_config* cfg,
+nvfp4_status nvfp4_amax(const void* x, nvfp4_dtype dtype_arg, int64_t rows, int64_t cols, const nvfp4_config* cfg,
                         float* amax_dev, void* workspace, size_t workspace_bytes, void* stream) {
-  if (rows < 0 || cols < 0) return NVFP4_ERR_SHAPE;
+  if (!dims_ok(rows, cols)) return NVFP4_ERR_SHAPE;
+  const int dtype = enum_bits(dtype_arg);
   if (dtype != NVFP4_IN_BF16 && dtype != NVFP4_IN_F32) return NVFP4_ERR_DTYPE;
   const bool rht = cfg && cfg->rht;
   if (rht && cols % 16) return NVFP4_ERR_SHAPE;
@@ -837,9 +861,10 @@ nvfp4_status nvfp4_amax(const void* x, nvfp4_dtype dtype, int64_t rows, int64_t 
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
-nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dtype, int64_t rows, int64_t cols, const nvfp4_config* cfg,
+nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dtype_arg, int64_t rows, int64_t cols, const nvfp4_config* cfg,
                             const float* amax_dev, const nvfp4_outputs* out, void* stream) {
   if (!cfg || !out || !amax_dev) return NVFP4_ERR_NULL;
+  const int dtype = enum_bits(dtype_arg);
   if (dtype != NVFP4_IN_BF16 && dtype != NVFP4_IN_F32) return NVFP4_ERR_DTYPE;
   if (cfg->block != NVFP4_BLOCK_1D && cfg->block != NVFP4_BLOCK_2D) return NVFP4_ERR_UNSUPPORTED;
   if (cfg->rule < NVFP4_RULE_NONE || cfg->rule > NVFP4_RULE_MAXERR) return NVFP4_ERR_UNSUPPORTED;
@@ -848,8 +873,9 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dtype, int64_t rows, int6
   const bool erow = cfg->emit_rowwise != 0, ecol = cfg->emit_colwise != 0;
   if (!erow && !ecol) return NVFP4_ERR_UNSUPPORTED;
   if (cfg->rht && (two_d || ecol)) return NVFP4_ERR_UNSUPPORTED;
-  if (rows < 0 || cols < 0) return NVFP4_ERR_SHAPE;
+  if (!dims_ok(rows, cols)) return NVFP4_ERR_SHAPE;
   if (cols % 16) return NVFP4_ERR_SHAPE;
+  if (!row_offset_ok(cfg->row_offset, rows, cols)) return NVFP4_ERR_SHAPE;
   if ((two_d || ecol) && rows % 16) return NVFP4_ERR_SHAPE;
   if ((two_d || ecol) && cols > kStripMaxCols) return NVFP4_ERR_SHAPE;
   const int64_t n = rows * cols;
@@ -865,12 +891,12 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dtype, int64_t rows, int6
   QuantParams p;
   p.amax = amax_dev;
   p.cap6 = 6.0f * cfg->scale_cap;
-  p.rht_mask = cfg->rht ? (cfg->rht_sign_mask & 0xFFFFu) : 0u;
+  p.rht_mask = cfg->rht ? (uint32_t)cfg->rht_sign_mask : 0u;
   p.k0 = (uint32_t)cfg->sr_seed;
   p.k1 = (uint32_t)(cfg->sr_seed >> 32);
   p.row_offset = cfg->row_offset;
   p.idx_base = cfg->row_offset * cols;
-  p.idx_below_2_34 = p.idx_base >= 0 && p.idx_base + rows * cols <= (1ll << 34);
+  p.idx_below_2_34 = p.idx_base + rows * cols <= (1ll << 34);
   p.emit_row = erow;
   p.emit_col = ecol;
   p.codes_row = out->codes_row;
@@ -921,9 +947,10 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dtype, int64_t rows, int6
 }
 
 nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale, int64_t rows,
-                              int64_t cols, nvfp4_block block, float* out, void* stream) {
+                              int64_t cols, nvfp4_block block_arg, float* out, void* stream) {
+  const int block = enum_bits(block_arg);
   if (block != NVFP4_BLOCK_1D && block != NVFP4_BLOCK_2D) return NVFP4_ERR_UNSUPPORTED;
-  if (rows < 0 || cols < 0 || cols % 16) return NVFP4_ERR_SHAPE;
+  if (!dims_ok(rows, cols) || cols % 16) return NVFP4_ERR_SHAPE;
   if (block == NVFP4_BLOCK_2D && rows % 16) return NVFP4_ERR_SHAPE;
   const int64_t n = rows * cols;
   if (n == 0) return NVFP4_OK;
@@ -940,13 +967,15 @@ nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
-nvfp4_status nvfp4_mxfp4_quantize(const void* x, nvfp4_dtype dtype, int64_t rows, int64_t cols,
+nvfp4_status nvfp4_mxfp4_quantize(const void* x, nvfp4_dtype dtype_arg, int64_t rows, int64_t cols,
                                   const nvfp4_mx_config* cfg, const nvfp4_mx_outputs* out, void* stream) {
   if (!cfg || !out) return NVFP4_ERR_NULL;
+  const int dtype = enum_bits(dtype_arg);
   if (dtype != NVFP4_IN_BF16 && dtype != NVFP4_IN_F32) return NVFP4_ERR_DTYPE;
   const bool erow = cfg->emit_rowwise != 0, ecol = cfg->emit_colwise != 0;
   if (!erow && !ecol) return NVFP4_ERR_UNSUPPORTED;
-  if (rows < 0 || cols < 0 || cols % 32) return NVFP4_ERR_SHAPE;
+  if (!dims_ok(rows, cols) || cols % 32) return NVFP4_ERR_SHAPE;
+  if (!row_offset_ok(cfg->row_offset, rows, cols)) return NVFP4_ERR_SHAPE;
   if (ecol && rows % 32) return NVFP4_ERR_SHAPE;
   if (ecol && cols > kStripMaxCols) return NVFP4_ERR_SHAPE;
   const int64_t n = rows * cols;
@@ -963,7 +992,7 @@ nvfp4_status nvfp4_mxfp4_quantize(const void* x, nvfp4_dtype dtype, int64_t rows
   p.k1 = (uint32_t)(cfg->sr_seed >> 32);
   p.row_offset = cfg->row_offset;
   p.idx_base = cfg->row_offset * cols;
-  p.idx_below_2_34 = p.idx_base >= 0 && p.idx_base + rows * cols <= (1ll << 34);
+  p.idx_below_2_34 = p.idx_base + rows * cols <= (1ll << 34);
   p.emit_row = erow;
   p.emit_col = ecol;
   p.codes_row = out->codes_row;
@@ -999,7 +1028,7 @@ nvfp4_status nvfp4_mxfp4_quantize(const void* x, nvfp4_dtype dtype, int64_t rows
 
 nvfp4_status nvfp4_mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                                     float* out, void* stream) {
-  if (rows < 0 || cols < 0 || cols % 32) return NVFP4_ERR_SHAPE;
+  if (!dims_ok(rows, cols) || cols % 32) return NVFP4_ERR_SHAPE;
   const int64_t n = rows * cols;
   if (n == 0) return NVFP4_OK;
   if (!codes || !scales || !out) return NVFP4_ERR_NULL;
@@ -1011,10 +1040,11 @@ nvfp4_status nvfp4_mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
-nvfp4_status nvfp4_error_stats(const void* x, nvfp4_dtype dtype, int64_t rows, int64_t cols, const nvfp4_config* cfg,
+nvfp4_status nvfp4_error_stats(const void* x, nvfp4_dtype dtype_arg, int64_t rows, int64_t cols, const nvfp4_config* cfg,
                                const float* amax_dev, float bin_width, int32_t nbins, double* stats_dev,
                                void* stream) {
   if (!cfg || !amax_dev || !stats_dev) return NVFP4_ERR_NULL;
+  const int dtype = enum_bits(dtype_arg);
   if (dtype != NVFP4_IN_BF16 && dtype != NVFP4_IN_F32) return NVFP4_ERR_DTYPE;
   if (cfg->block != NVFP4_BLOCK_1D && cfg->block != NVFP4_BLOCK_2D) return NVFP4_ERR_UNSUPPORTED;
   if (cfg->rule < NVFP4_RULE_NONE || cfg->rule > NVFP4_RULE_MAXERR) return NVFP4_ERR_UNSUPPORTED;
@@ -1024,14 +1054,14 @@ nvfp4_status nvfp4_error_stats(const void* x, nvfp4_dtype dtype, int64_t rows, i
   if (nbins < 1 || nbins > kMaxBins) return NVFP4_ERR_UNSUPPORTED;
   int ex = 0;
   if (!(bin_width > 0.0f) || frexpf(bin_width, &ex) != 0.5f || ex < -100 || ex > 100) return NVFP4_ERR_UNSUPPORTED;
-  if (rows < 0 || cols < 0 || rows % 16 || cols % 16) return NVFP4_ERR_SHAPE;
+  if (!dims_ok(rows, cols) || rows % 16 || cols % 16) return NVFP4_ERR_SHAPE;
   const int64_t n = rows * cols;
   if (n > 0 && !x) return NVFP4_ERR_NULL;
   if (n > 0 && !aligned16(x)) return NVFP4_ERR_ALIGN;
   QuantParams p{};
   p.amax = amax_dev;
   p.cap6 = 6.0f * cfg->scale_cap;
-  p.rht_mask = cfg->rht ? (cfg->rht_sign_mask & 0xFFFFu) : 0u;
+  p.rht_mask = cfg->rht ? (uint32_t)cfg->rht_sign_mask : 0u;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(zero_f64_kernel, dim3(1), dim3(kThreads), 0, s, stats_dev, 3 * nbins);
   const int64_t nreg = (rows / 16) * (cols / 16);

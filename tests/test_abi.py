@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert nv.abi_version() == 1
+    assert nv.abi_version() == 2
     for s in range(8):
         assert nv.lib().nvfp4_status_string(s)
 
@@ -158,3 +158,102 @@ def test_gemm_validation():
     assert L.nvfp4_mxfp4_gemm(f, f, f, f, 64, 64, 192, f, None) == nv.ERR_SHAPE
     assert L.nvfp4_mxfp4_gemm(None, f, f, f, 64, 64, 256, f, None) == nv.ERR_NULL
     assert L.nvfp4_mxfp4_gemm(f, f, P(FAKE + 4), f, 64, 64, 256, f, None) == nv.ERR_ALIGN
+
+
+# ------------------------------------------------ binding argument checks ----
+# The C ABI cannot see buffer sizes, so the binding checks every tensor before
+# calling it.  Device checks come last, which lets these CPU tests reach each
+# shape/dtype rejection; a call whose tensors are all well formed but on the
+# CPU ends in the "no CPU path" error.
+
+def _t(*shape, dtype=None):
+    torch = pytest.importorskip("torch")
+    return torch.zeros(shape, dtype=dtype or torch.uint8)
+
+
+def test_binding_quantize_checks_every_buffer():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(32, 64, dtype=torch.bfloat16)
+    a = torch.zeros(1, dtype=torch.float32)
+    good = nv.allocate_outputs(32, 64, "1d", True, True, "cpu")
+    with pytest.raises(TypeError, match="GPU"):
+        nv.quantize(x, a, colwise=True, out=good)
+    with pytest.raises(TypeError, match="amax_t"):
+        nv.quantize(x, a.double(), out=good)
+    with pytest.raises(ValueError, match="amax_t"):
+        nv.quantize(x, torch.zeros(0, dtype=torch.float32), out=good)
+    for key, bad in (("codes_row", _t(32, 16)), ("scales_row", _t(32, 2)), ("codes_col", _t(64, 8)),
+                     ("scales_col", _t(4, 2)), ("codes_row", _t(32, 32, dtype=torch.int8))):
+        o = dict(good)
+        o[key] = bad
+        with pytest.raises((ValueError, TypeError), match=key):
+            nv.quantize(x, a, colwise=True, out=o)
+    o = dict(good)
+    del o["codes_col"]
+    with pytest.raises(ValueError, match="codes_col"):
+        nv.quantize(x, a, colwise=True, out=o)
+    # a 2D row copy has one scale per tile: the 1D-shaped scales are refused
+    with pytest.raises(ValueError, match="scales_row"):
+        nv.quantize(x, a, block="2d", out=good)
+    with pytest.raises(ValueError, match="contiguous"):
+        nv.quantize(x.t(), a)
+    with pytest.raises(TypeError):
+        nv.quantize(x.to(torch.float16), a)
+    with pytest.raises(ValueError, match="16-bit"):
+        nv.quantize(x, a, rht=True, rht_mask=0x1FFFF)
+    with pytest.raises(ValueError, match="rule"):
+        nv.quantize(x, a, rule="l2")
+
+
+def test_binding_amax_dequantize_error_stats_checks():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(32, 64, dtype=torch.float32)
+    with pytest.raises(ValueError, match="workspace"):
+        nv.amax(x, workspace=torch.zeros(0, dtype=torch.uint8))
+    with pytest.raises(TypeError, match="out"):
+        nv.amax(x, out=torch.zeros(1, dtype=torch.float64))
+    with pytest.raises(TypeError, match="GPU"):
+        nv.amax(x, out=torch.zeros(1), workspace=torch.zeros(4096, dtype=torch.uint8))
+    ts = torch.zeros(1)
+    with pytest.raises(ValueError, match="codes"):
+        nv.dequantize(_t(32, 16), _t(32, 4), ts, 32, 64)      # rows/cols disagree with codes.shape
+    with pytest.raises(ValueError, match="scales"):
+        nv.dequantize(_t(32, 32), _t(32, 4), ts, 32, 64, block="2d")
+    with pytest.raises(ValueError, match="out"):
+        nv.dequantize(_t(32, 32), _t(32, 4), ts, 32, 64, out=torch.zeros(32, 32))
+    with pytest.raises(TypeError, match="tensor_scale"):
+        nv.dequantize(_t(32, 32), _t(32, 4), ts.half(), 32, 64)
+    with pytest.raises(TypeError, match="GPU"):
+        nv.dequantize(_t(32, 32), _t(32, 4), ts, 32, 64)
+    a = torch.zeros(1)
+    with pytest.raises(ValueError, match="out"):
+        nv.error_stats(x, a, nbins=8, out=torch.zeros(3, 9, dtype=torch.float64))
+    with pytest.raises(ValueError, match="nbins"):
+        nv.error_stats(x, a, nbins=65)
+
+
+def test_binding_mxfp4_and_gemm_checks():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(64, 64, dtype=torch.bfloat16)
+    good = nv.mxfp4_allocate_outputs(64, 64, True, True, "cpu")
+    o = dict(good)
+    o["scales_col"] = _t(64, 4)
+    with pytest.raises(ValueError, match="scales_col"):
+        nv.mxfp4_quantize(x, colwise=True, out=o)
+    with pytest.raises(TypeError, match="GPU"):
+        nv.mxfp4_quantize(x, colwise=True, out=good)
+    with pytest.raises(ValueError, match="scales"):
+        nv.mxfp4_dequantize(_t(64, 32), _t(64, 4), 64, 64)
+    ts = torch.zeros(1)
+    with pytest.raises(ValueError, match="same K"):
+        nv.gemm(_t(64, 64), _t(64, 8), ts, _t(64, 32), _t(64, 4), ts)
+    with pytest.raises(ValueError, match="b_scales"):
+        nv.gemm(_t(64, 64), _t(64, 8), ts, _t(64, 64), _t(64, 8), ts, b_block="2d")
+    with pytest.raises(ValueError, match="out"):
+        nv.gemm(_t(64, 64), _t(64, 8), ts, _t(32, 64), _t(32, 8), ts, out=torch.zeros(64, 64))
+    with pytest.raises(TypeError, match="GPU"):
+        nv.gemm(_t(64, 64), _t(64, 8), ts, _t(32, 64), _t(32, 8), ts)
+    with pytest.raises(ValueError, match="a_scales"):
+        nv.mxfp4_gemm(_t(64, 64), _t(64, 8), _t(32, 64), _t(32, 4))
+    with pytest.raises(TypeError, match="GPU"):
+        nv.mxfp4_gemm(_t(64, 64), _t(64, 4), _t(32, 64), _t(32, 4))

@@ -203,13 +203,34 @@ def _assert_same(tag, key, got: np.ndarray, ref: np.ndarray) -> None:
         raise AssertionError(f"{tag}: {key} differs at {len(bad)} places, first {bad[:5].tolist()}")
 
 
-@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, "5plain"])
+# Several full 256-row strips plus a partial last strip (the strip kernel's
+# partial write-out of codes and scales), with 4/6 and stochastic rounding.
+MULTI_STRIP = [(272, 208), (320, 80), (528, 208)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("path", ["1d-row-col", "2d-row-col"])
+@pytest.mark.parametrize("rows,cols", MULTI_STRIP)
+def test_multi_strip_sr_four_over_six(rows, cols, path, dtype):
+    k = 5 if dtype == "bf16" else 1
+    c = workloads.config(k, rows, cols, block="2d" if path.startswith("2d") else "1d", emit_row=True,
+                         emit_col=True, rht=False, sr=True, sr_seed=41, rule="mae", cap=256.0)
+    x = workloads.generate(k, rows, cols, seed=12)
+    compare_all(x, c, f"strips-{rows}x{cols}-{path}-{dtype}")
+
+
+FULL = {1: workloads.CONFIGS[1], 2: workloads.CONFIGS[2], 3: workloads.CONFIGS[3], 4: workloads.CONFIGS[4],
+        5: workloads.CONFIGS[5], "5plain": workloads.CONFIG5_PLAIN, "2plain": workloads.CONFIG2_PLAIN,
+        "3sr": workloads.CONFIG3_SR}
+
+
+@pytest.mark.parametrize("k", list(FULL))
 def test_full_size_workloads_whole(k):
     """Every output byte of the full-size workloads against the oracle (row
     bands of the oracle run on up to 16 host threads; blocks are independent,
     so threading does not change its bits), then a rerun that must write the
     same bytes."""
-    c = with_mask(workloads.CONFIG5_PLAIN if k == "5plain" else workloads.CONFIGS[k])
+    c = with_mask(FULL[k])
     rows, cols = c["rows"], c["cols"]
     tag = f"full workload {k}"
     say(f"{tag}: generating {rows}x{cols}")

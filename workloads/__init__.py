@@ -81,6 +81,15 @@ CONFIGS = {
 CONFIG5_PLAIN = dict(CONFIGS[5], name="65536x8192 bf16, 1x16 row + col copies, SR seed 7, no 4/6, cap 448",
                      rule="none", cap=448.0)
 
+# Config 2 with 4/6 off (cap 448): the secondary 4/6-cost point (row copy only).
+CONFIG2_PLAIN = dict(CONFIGS[2], name="8192x4096 bf16 activation, 1x16 rows, no 4/6, RNE, cap 448",
+                     rule="none", cap=448.0)
+
+# The weight with Four Over Six and stochastic rounding on its 16x16 tiles, both
+# copies (activations, weights and gradients all in 4/6 format).
+CONFIG3_SR = dict(CONFIGS[3], name="5120x20480 bf16 weight, 16x16 tiles, row + col copies, 4/6 MAE, SR seed 5, "
+                                   "cap 256", rule="mae", sr=True, sr_seed=5, cap=256.0)
+
 
 def config(k: int, rows: int | None = None, cols: int | None = None, **overrides) -> dict:
     """A copy of workload k, optionally at another shape (same recipe and options)."""
