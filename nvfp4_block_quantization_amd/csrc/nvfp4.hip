@@ -247,7 +247,7 @@ struct RowChunk {
     }
   }
   __device__ __forceinline__ void process(int64_t c, int64_t nblocks, const QuantParams& p, const f32x2* tab,
-                                          const TensorScale& ts) const {
+                                          const TensorScale& ts, const PhiloxKey& key) const {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t b = block(c, u);
@@ -259,9 +259,9 @@ struct RowChunk {
       if constexpr (SR) {
         const uint64_t idx0 = (uint64_t)p.idx_base + (uint64_t)(16 * b);
         if (p.idx_below_2_34) {  // uniform
-          sr_words16_hi_uniform((uint32_t)(idx0 >> 2), 0u, p.k0, p.k1, w);
+          sr_words16_hi_uniform((uint32_t)(idx0 >> 2), 0u, key, w);
         } else {
-          sr_words16(idx0, p.k0, p.k1, w);
+          sr_words16(idx0, key, w);
         }
       }
       if constexpr (MX) {
@@ -290,14 +290,15 @@ __global__ __launch_bounds__(kThreads) void quant_row_kernel(const void* __restr
   const int64_t per_chunk = (int64_t)kThreads * U;
   const int64_t nchunks = (nblocks + per_chunk - 1) / per_chunk;
   const int64_t G = gridDim.x;
+  const PhiloxKey key = philox_key(p.k0, p.k1);
   RowChunk<DT, RHT, SR, RULE, U, MX> A, B;
   int64_t c = blockIdx.x;
   if (c < nchunks) A.load(x, c, nblocks);
   for (; c < nchunks; c += 2 * G) {
     if (c + G < nchunks) B.load(x, c + G, nblocks);
-    A.process(c, nblocks, p, tab, ts);
+    A.process(c, nblocks, p, tab, ts, key);
     if (c + 2 * G < nchunks) A.load(x, c + 2 * G, nblocks);
-    if (c + G < nchunks) B.process(c + G, nblocks, p, tab, ts);
+    if (c + G < nchunks) B.process(c + G, nblocks, p, tab, ts, key);
   }
 }
 
@@ -315,6 +316,21 @@ __global__ __launch_bounds__(kThreads) void quant_row_kernel(const void* __restr
 // the four strips that share the row copy's 128-byte lines run back to back
 // on one XCD and meet in its L2.
 constexpr int kStripRows = 256;
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// A raw buffer resource over `bytes` bytes at `base`: accesses at offsets past
+// the range are dropped by the hardware (stores) or return zero (loads).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+}
+
+// Wave-private LDS exchange: wait until this wave's LDS accesses have completed
+// and keep the compiler from moving memory operations across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt untouched
+  __builtin_amdgcn_wave_barrier();
+}
 constexpr int64_t kStripMaxCols = 1ll << 24;  // column copies and 16x16 tiles: at most 2^24 columns
 
 __device__ __forceinline__ uint32_t xcd_order(uint32_t bid, uint32_t nb) {
@@ -361,6 +377,7 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
   const uint32_t sy = strip / strips_x, sx = strip - sy * strips_x;
   const int t = threadIdx.x, g = t >> 4, i = t & 15;
   const int bi = g >> 2, bj = g & 3;
+  const PhiloxKey key = philox_key(p.k0, p.k1);
   const int64_t sr0 = (int64_t)sy * kStripRows;           // first row of the strip
   const int64_t c0 = (int64_t)sx * 64 + 16 * bj;          // first column of this lane's blocks
   const int64_t rows_left = rows - sr0;
@@ -392,11 +409,16 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
   TensorScale ts{};
   if constexpr (!MX) ts = workgroup_setup(p, tab);
 
-  // One 64x64 sub-tile whose uniform element base is eq; prefetches sub-tile q + 1 into `nxt`.
-  auto sub_tile = [&](int q, int64_t eq, const RawBlock<DT>& raw, RawBlock<DT>& nxt) {
+  // One 64x64 sub-tile whose uniform element base is eq; prefetches sub-tile q + 1 into `nxt`
+  // (PF: 1 = always, 0 = never, -1 = when q + 1 < nsub).
+  auto sub_tile = [&](auto PF, int q, int64_t eq, const RawBlock<DT>& raw, RawBlock<DT>& nxt) {
     const int64_t r0 = sr0 + 64 * q + 16 * bi;  // first row of this lane's 16x16 block
     const bool valid = lane_valid(q);
-    if (q + 1 < nsub) load_sub(q + 1, eq + e_step, nxt);
+    if constexpr (decltype(PF)::value == 1) {
+      load_sub(q + 1, eq + e_step, nxt);
+    } else if constexpr (decltype(PF)::value == -1) {
+      if (q + 1 < nsub) load_sub(q + 1, eq + e_step, nxt);
+    }
 
     // ---- row pass: lane i holds row r0 + i, columns c0 .. c0 + 15 (element index eq + L ..)
     float y[16];
@@ -408,9 +430,9 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
       // the high word is uniform and the low word a 32-bit add
       const uint64_t qu = (uint64_t)(eq + p.idx_base) >> 2;
       if ((uint64_t)(uint32_t)qu + (lmax >> 2) + 3u < (1ull << 32)) {
-        sr_words16_hi_uniform((uint32_t)qu + (L >> 2), (uint32_t)(qu >> 32), p.k0, p.k1, w);
+        sr_words16_hi_uniform((uint32_t)qu + (L >> 2), (uint32_t)(qu >> 32), key, w);
       } else {
-        sr_words16((uint64_t)(eq + p.idx_base) + L, p.k0, p.k1, w);
+        sr_words16((uint64_t)(eq + p.idx_base) + L, key, w);
       }
     }
     BlockResult res;
@@ -426,14 +448,30 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
       res = quant_block16<SR, RULE>(y, w, tab, ts.den6, ts.den4);
     }
 
-    if (valid && p.emit_row) {  // eq is a multiple of 64 (MXFP4: cols % 32 == 0, so of 32 per row too)
-      *reinterpret_cast<uint2*>(p.codes_row + (eq >> 1) + (L >> 1)) = make_uint2(res.codes.lo, res.codes.hi);
+    {
+      // Row copy through buffer stores: a lane that stores nothing gets an offset
+      // beyond the resource's range, which the hardware drops, so every lane (and
+      // every path) issues the same stores and the waits for the prefetched
+      // sub-tile count them exactly.  Resources cover this sub-tile's 64 rows.
+      constexpr uint32_t kDrop = 0xFFFFFFF0u;
+      const bool er = p.emit_row != 0;
+      const int64_t srow = (sr0 + 64 * q) / 16;  // first 16-row block row of the sub-tile
+      const __amdgpu_buffer_rsrc_t rc = raw_rsrc(er ? p.codes_row + (eq >> 1) : nullptr,
+                                                 er ? (uint32_t)(64 * (cols / 2)) : 0u);
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{res.codes.lo, res.codes.hi}, rc, valid ? (L >> 1) : kDrop, 0, 0);
       if constexpr (MX) {
-        if ((bj & 1) == 0) p.scales_row[(eq >> 5) + (L >> 5)] = (uint8_t)res.sb;
+        const __amdgpu_buffer_rsrc_t rs = raw_rsrc(er ? p.scales_row + (eq >> 5) : nullptr,
+                                                   er ? (uint32_t)(64 * (cols / 32)) : 0u);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)res.sb, rs, (valid && (bj & 1) == 0) ? (L >> 5) : kDrop, 0, 0);
       } else if constexpr (TWO_D) {
-        if (i == 0) p.scales_row[(r0 / 16) * (cols / 16) + c0 / 16] = (uint8_t)res.sb;
+        const __amdgpu_buffer_rsrc_t rs = raw_rsrc(er ? p.scales_row + srow * (cols / 16) + (int64_t)sx * 4 : nullptr,
+                                                   er ? (uint32_t)(4 * (cols / 16)) : 0u);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)res.sb, rs,
+                                             (valid && i == 0) ? (uint32_t)(bi * (cols / 16) + bj) : kDrop, 0, 0);
       } else {
-        p.scales_row[(eq >> 4) + (L >> 4)] = (uint8_t)res.sb;
+        const __amdgpu_buffer_rsrc_t rs = raw_rsrc(er ? p.scales_row + (eq >> 4) : nullptr,
+                                                   er ? (uint32_t)(64 * (cols / 16)) : 0u);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)res.sb, rs, valid ? (L >> 4) : kDrop, 0, 0);
       }
     }
     if (!p.emit_col) return;  // uniform across the workgroup
@@ -459,7 +497,11 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
         for (int k = 0; k < 16; ++k) dw[k] = w[k];
       }
     }
-    __syncthreads();
+    if constexpr (MX) {
+      __syncthreads();
+    } else {
+      wave_lds_sync();  // the staged band is this wave's own
+    }
 
     // ---- column pass: lane i holds column 16 * bj + i, rows r0 .. r0 + 15
     const int col = 16 * bj + i;
@@ -479,7 +521,11 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
       mcol = absmax16(y);
       lds_m[bi * 64 + col] = mcol;
     }
-    __syncthreads();  // the next sub-tile overwrites the staging area
+    if constexpr (MX) {
+      __syncthreads();  // the next sub-tile overwrites the staging area
+    } else {
+      wave_lds_sync();
+    }
     BlockCodes cc;
     uint32_t sbc;
     if constexpr (MX) {
@@ -514,12 +560,24 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
     }
   };
 
-  // Two sub-tiles per trip so that the prefetch buffers alternate without copies.
-  int64_t eq = e_first;
-  for (int q = 0; q < nsub; q += 2) {  // uniform trip count
-    sub_tile(q, eq, buf0, buf1);
-    if (q + 1 < nsub) sub_tile(q + 1, eq + e_step, buf1, buf0);
-    eq += 2 * e_step;
+  using PF_ALWAYS = std::integral_constant<int, 1>;
+  using PF_NEVER = std::integral_constant<int, 0>;
+  using PF_IF = std::integral_constant<int, -1>;
+  if (nsub == 4) {
+    // a full strip: straight-line code, so that every wait for a prefetched
+    // sub-tile counts exactly the memory operations issued after it
+    sub_tile(PF_ALWAYS{}, 0, e_first, buf0, buf1);
+    sub_tile(PF_ALWAYS{}, 1, e_first + e_step, buf1, buf0);
+    sub_tile(PF_ALWAYS{}, 2, e_first + 2 * e_step, buf0, buf1);
+    sub_tile(PF_NEVER{}, 3, e_first + 3 * e_step, buf1, buf0);
+  } else {
+    // Two sub-tiles per trip so that the prefetch buffers alternate without copies.
+    int64_t eq = e_first;
+    for (int q = 0; q < nsub; q += 2) {  // uniform trip count
+      sub_tile(PF_IF{}, q, eq, buf0, buf1);
+      if (q + 1 < nsub) sub_tile(PF_IF{}, q + 1, eq + e_step, buf1, buf0);
+      eq += 2 * e_step;
+    }
   }
   if (!p.emit_col) return;
   __syncthreads();

@@ -36,7 +36,11 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4 v, float* y) {
 // encoding for every binary32 r in [0, 448); above 448 it does not saturate,
 // so r is clamped first (448 itself encodes as 0x7E).
 __device__ __forceinline__ uint32_t e4m3_encode(float r) {
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(r, 448.0f), 0.0f, 0, false) & 0xFFu;
+  // r is +0, positive, +inf or NaN: for these the unsigned minimum of the bit
+  // patterns with 448's is the saturated value (and the float minimum where both are
+  // numbers), so overflowing and NaN quotients encode as 448 too
+  const uint32_t c = min(__float_as_uint(r), 0x43E00000u);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(c), 0.0f, (int)c, false) & 0xFFu;
 }
 
 __device__ __forceinline__ float e4m3_decode(uint32_t c) {
@@ -105,101 +109,107 @@ __device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
   return d;
 }
 
-// Philox-4x32-10 (Salmon et al., SC'11).  Keys are wave-uniform.
-struct U4 {
-  uint32_t x, y, z, w;
+// Philox-4x32-10 (Salmon et al., SC'11): ten rounds, each two 32x32->64
+// products with the published multipliers and xors with the round key.  The
+// round keys are the key advanced by the published Weyl constants before each
+// round after the first (wave-uniform, computed once per kernel).
+struct PhiloxKey {
+  uint32_t k0[10], k1[10];
 };
 
-__device__ __forceinline__ U4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
-                                            uint32_t k1) {
+__device__ __forceinline__ PhiloxKey philox_key(uint32_t k0, uint32_t k1) {
+  PhiloxKey K;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
-    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-    const uint32_t n0 = xor3((uint32_t)(p1 >> 32), c1, k0);
-    const uint32_t n2 = xor3((uint32_t)(p0 >> 32), c3, k1);
-    c1 = (uint32_t)p1;
-    c3 = (uint32_t)p0;
-    c0 = n0;
-    c2 = n2;
-    k0 += 0x9E3779B9u;
-    k1 += 0xBB67AE85u;
+    K.k0[r] = k0 + (uint32_t)r * 0x9E3779B9u;
+    K.k1[r] = k1 + (uint32_t)r * 0xBB67AE85u;
   }
-  return U4{c0, c1, c2, c3};
+  return K;
 }
 
-// Philox-4x32-10 for counters (c0, c1, 0, 0) whose high word c1 is the same
-// for the whole wave: the first round's second product is zero and its xor of
-// c1 with the key is wave-uniform, so the second round's first product and the
-// third round's c3 term are uniform too and run on the scalar unit.  Same
-// results as philox4x32_10(c0, c1, 0, 0, k0, k1).
-__device__ __forceinline__ U4 philox4x32_10_hi_uniform(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1) {
-  // round 1 (c2 = c3 = 0)
-  uint64_t p0 = (uint64_t)0xD2511F53u * c0;
-  uint32_t n0 = c1 ^ k0;                       // uniform
-  uint32_t n2 = (uint32_t)(p0 >> 32) ^ k1;
-  uint32_t x1 = 0u, x3 = (uint32_t)p0;
-  k0 += 0x9E3779B9u;
-  k1 += 0xBB67AE85u;
-  // round 2 (c0 = n0 uniform, c1 = 0)
-  uint64_t pu = (uint64_t)0xD2511F53u * n0;    // uniform
-  uint64_t p1 = (uint64_t)0xCD9E8D57u * n2;
-  uint32_t m0 = (uint32_t)(p1 >> 32) ^ k0;
-  uint32_t m2 = x3 ^ ((uint32_t)(pu >> 32) ^ k1);
-  x1 = (uint32_t)p1;
-  x3 = (uint32_t)pu;                           // uniform
-  k0 += 0x9E3779B9u;
-  k1 += 0xBB67AE85u;
-  // round 3 (c3 uniform)
-  p0 = (uint64_t)0xD2511F53u * m0;
-  p1 = (uint64_t)0xCD9E8D57u * m2;
-  uint32_t c0n = xor3((uint32_t)(p1 >> 32), x1, k0);
-  uint32_t c2n = (uint32_t)(p0 >> 32) ^ (x3 ^ k1);
-  uint32_t c1n = (uint32_t)p1, c3n = (uint32_t)p0;
-  k0 += 0x9E3779B9u;
-  k1 += 0xBB67AE85u;
+// Rounds r0 .. 9 of four instances advanced together (round-major, so that no
+// product waits for the one just before it).
+__device__ __forceinline__ void philox_rounds4(uint32_t* x0, uint32_t* x1, uint32_t* x2, uint32_t* x3,
+                                               const PhiloxKey& K, int r0) {
 #pragma unroll
-  for (int r = 3; r < 10; ++r) {
-    const uint64_t q0 = (uint64_t)0xD2511F53u * c0n;
-    const uint64_t q1 = (uint64_t)0xCD9E8D57u * c2n;
-    const uint32_t a = xor3((uint32_t)(q1 >> 32), c1n, k0);
-    const uint32_t b = xor3((uint32_t)(q0 >> 32), c3n, k1);
-    c1n = (uint32_t)q1;
-    c3n = (uint32_t)q0;
-    c0n = a;
-    c2n = b;
-    k0 += 0x9E3779B9u;
-    k1 += 0xBB67AE85u;
+  for (int r = r0; r < 10; ++r) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint64_t p0 = (uint64_t)0xD2511F53u * x0[j];
+      const uint64_t p1 = (uint64_t)0xCD9E8D57u * x2[j];
+      const uint32_t n0 = xor3((uint32_t)(p1 >> 32), x1[j], K.k0[r]);
+      const uint32_t n2 = xor3((uint32_t)(p0 >> 32), x3[j], K.k1[r]);
+      x1[j] = (uint32_t)p1;
+      x3[j] = (uint32_t)p0;
+      x0[j] = n0;
+      x2[j] = n2;
+    }
   }
-  return U4{c0n, c1n, c2n, c3n};
 }
 
 // Words for 16 consecutive elements whose first Philox counter is (lo, hi)
-// with lo + 3 < 2^32: counters (lo + j, hi, 0, 0), j = 0..3.
-__device__ __forceinline__ void sr_words16_hi_uniform(uint32_t lo, uint32_t hi, uint32_t k0, uint32_t k1,
-                                                      uint32_t* w) {
+// with lo + 3 < 2^32 and hi wave-uniform: counters (lo + j, hi, 0, 0).  The
+// first round's second product is zero and its xor of hi with the key is
+// uniform, so the second round's first product and the third round's x3 term
+// are uniform too and run on the scalar unit.  Same words as four full
+// Philox-4x32-10 evaluations.
+__device__ __forceinline__ void sr_words16_hi_uniform(uint32_t lo, uint32_t hi, const PhiloxKey& K, uint32_t* w) {
+  uint32_t x0[4], x1[4], x2[4], x3[4];
+  const uint32_t u0 = hi ^ K.k0[0];                       // round 1: x0, uniform
+  const uint64_t pu = (uint64_t)0xD2511F53u * u0;         // round 2: first product, uniform
+  const uint32_t hu = (uint32_t)(pu >> 32) ^ K.k1[1];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const U4 r = philox4x32_10_hi_uniform(lo + j, hi, k0, k1);
-    w[4 * j + 0] = r.x;
-    w[4 * j + 1] = r.y;
-    w[4 * j + 2] = r.z;
-    w[4 * j + 3] = r.w;
+    const uint64_t p = (uint64_t)0xD2511F53u * (lo + (uint32_t)j);  // round 1
+    const uint32_t a2 = (uint32_t)(p >> 32) ^ K.k1[0];
+    const uint32_t a3 = (uint32_t)p;
+    const uint64_t q = (uint64_t)0xCD9E8D57u * a2;                   // round 2 (x1 = 0)
+    x0[j] = (uint32_t)(q >> 32) ^ K.k0[1];
+    x1[j] = (uint32_t)q;
+    x2[j] = a3 ^ hu;
+  }
+  const uint32_t u3 = (uint32_t)pu ^ K.k1[2];             // round 3: x3 uniform
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * x0[j];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * x2[j];
+    const uint32_t n0 = xor3((uint32_t)(p1 >> 32), x1[j], K.k0[2]);
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ u3;
+    x1[j] = (uint32_t)p1;
+    x3[j] = (uint32_t)p0;
+    x0[j] = n0;
+    x2[j] = n2;
+  }
+  philox_rounds4(x0, x1, x2, x3, K, 3);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    w[4 * j + 0] = x0[j];
+    w[4 * j + 1] = x1[j];
+    w[4 * j + 2] = x2[j];
+    w[4 * j + 3] = x3[j];
   }
 }
 
 // Words for 16 consecutive elements starting at idx0 (idx0 % 4 == 0):
 // element idx uses word (idx mod 4) of the block at counter (idx/4, 0, 0).
-__device__ __forceinline__ void sr_words16(uint64_t idx0, uint32_t k0, uint32_t k1, uint32_t* w) {
+__device__ __forceinline__ void sr_words16(uint64_t idx0, const PhiloxKey& K, uint32_t* w) {
   const uint64_t q0 = idx0 >> 2;
+  uint32_t x0[4], x1[4], x2[4], x3[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint64_t q = q0 + j;
-    const U4 r = philox4x32_10((uint32_t)q, (uint32_t)(q >> 32), 0u, 0u, k0, k1);
-    w[4 * j + 0] = r.x;
-    w[4 * j + 1] = r.y;
-    w[4 * j + 2] = r.z;
-    w[4 * j + 3] = r.w;
+    const uint64_t q = q0 + (uint64_t)j;
+    x0[j] = (uint32_t)q;
+    x1[j] = (uint32_t)(q >> 32);
+    x2[j] = 0u;
+    x3[j] = 0u;
+  }
+  philox_rounds4(x0, x1, x2, x3, K, 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    w[4 * j + 0] = x0[j];
+    w[4 * j + 1] = x1[j];
+    w[4 * j + 2] = x2[j];
+    w[4 * j + 3] = x3[j];
   }
 }
 
@@ -337,15 +347,19 @@ __device__ __forceinline__ uint32_t sr_pair_byte(uint32_t d, const float* y, int
 }
 
 __device__ __forceinline__ void sr_pair_regs(const float* y, float e6, float e4, const uint32_t* w, uint32_t* P) {
+  // register r holds elements k0(r), k0(r) + 2, + 4, + 6 with k0(r) = 8 (r >> 1) + (r & 1);
+  // the four registers' convert chains are interleaved byte by byte
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int k0 = (r >> 1) * 8 + (r & 1);  // elements k0, k0 + 2, k0 + 4, k0 + 6
-    uint32_t d = cvt_sr_byte0_fresh(f32x2{y[k0] * e6, y[k0] * e4}, w[k0]);
-    d = sr_pair_byte<1>(d, y, k0 + 2, e6, e4, w);
-    d = sr_pair_byte<2>(d, y, k0 + 4, e6, e4, w);
-    d = sr_pair_byte<3>(d, y, k0 + 6, e6, e4, w);
-    P[r] = d;
+    const int k0 = (r >> 1) * 8 + (r & 1);
+    P[r] = cvt_sr_byte0_fresh(f32x2{y[k0] * e6, y[k0] * e4}, w[k0]);
   }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) P[r] = sr_pair_byte<1>(P[r], y, (r >> 1) * 8 + (r & 1) + 2, e6, e4, w);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) P[r] = sr_pair_byte<2>(P[r], y, (r >> 1) * 8 + (r & 1) + 4, e6, e4, w);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) P[r] = sr_pair_byte<3>(P[r], y, (r >> 1) * 8 + (r & 1) + 6, e6, e4, w);
 }
 
 // (a & 0x0F0F0F0F) | (b & 0xF0F0F0F0): one v_bfi_b32.
@@ -469,8 +483,8 @@ __device__ __forceinline__ float divide(float m, const Divisor& d) {
     const float r0 = __builtin_fmaf(-q0, d.den, m);
     const float q1 = __builtin_fmaf(r0, d.y, q0);
     const float r1 = __builtin_fmaf(-q1, d.den, m);
-    const float q2 = __builtin_fmaf(r1, d.y, q1);
-    return q0 < 1048576.0f ? q2 : q0;
+    // where m / den overflows, q0 is +inf and q2 NaN; e4m3_encode saturates both
+    return __builtin_fmaf(r1, d.y, q1);
   }
   return (m == 0.0f || d.den == 0.0f) ? 0.0f : __fdiv_rn(m, d.den);
 }
