@@ -19,7 +19,8 @@
  * Conventions for every entry point:
  *   - Tensors are row-major rows x cols (cols contiguous).  All data pointers
  *     are DEVICE pointers owned by the caller; the library allocates nothing
- *     and keeps no mutable global state.
+ *     and keeps no mutable global state (except the per-GPU scratch array of
+ *     nvfp4_amax_noalloc, described there).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Work is enqueued asynchronously on it; results are ready when the stream
  *     is synchronised.
@@ -112,6 +113,19 @@ size_t nvfp4_amax_workspace_bytes(int64_t rows, int64_t cols);
  * An empty tensor (rows or cols == 0) gives amax 0.  With rht, cols % 16 == 0. */
 nvfp4_status nvfp4_amax(const void* x, nvfp4_dtype dtype, int64_t rows, int64_t cols, const nvfp4_config* cfg,
                         float* amax_dev, void* workspace, size_t workspace_bytes, void* stream);
+
+/* nvfp4_amax without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, kernels and result as nvfp4_amax; the partial
+ * maxima go to a 4 KB array the library keeps in each GPU's memory until the
+ * process ends (nothing is allocated by the call; any tensor size is accepted,
+ * since the number of partials is capped).  Every call on one GPU shares that
+ * array: calls that overlap on one GPU (different streams or threads) race, and
+ * must be ordered by the caller.  NVFP4_ERR_HIP if the array's address cannot be
+ * obtained on the stream's device; NVFP4_ERR_UNSUPPORTED for device ordinals
+ * of 64 and above. */
+nvfp4_status nvfp4_amax_noalloc(const void* x, nvfp4_dtype dtype, int64_t rows, int64_t cols,
+                                const nvfp4_config* cfg, float* amax_dev, void* stream);
 
 /* Quantize x into NVFP4 with one fused pass over the input.
  * Per block (1x16 row block, 16x1 column block, or 16x16 tile):

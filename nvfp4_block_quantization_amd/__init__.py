@@ -98,6 +98,8 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_amax_workspace_bytes.argtypes = [i64, i64]
         L.nvfp4_amax.restype = i32
         L.nvfp4_amax.argtypes = [P, i32, i64, i64, ctypes.POINTER(Config), P, P, ctypes.c_size_t, P]
+        L.nvfp4_amax_noalloc.restype = i32
+        L.nvfp4_amax_noalloc.argtypes = [P, i32, i64, i64, ctypes.POINTER(Config), P, P]
         L.nvfp4_quantize.restype = i32
         L.nvfp4_quantize.argtypes = [P, i32, i64, i64, ctypes.POINTER(Config), P, ctypes.POINTER(Outputs), P]
         L.nvfp4_dequantize.restype = i32
@@ -223,6 +225,23 @@ def amax(x: torch.Tensor, rht: bool = False, rht_mask: int = 0, out: torch.Tenso
     st = lib().nvfp4_amax(_ptr(x), _dtype_code(x), rows, cols, ctypes.byref(cfg), _ptr(out), _ptr(workspace),
                           workspace.numel(), _stream(dev, stream))
     _check(st, "nvfp4_amax")
+    return out
+
+
+def amax_noalloc(x: torch.Tensor, rht: bool = False, rht_mask: int = 0, out: torch.Tensor | None = None,
+                 stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """nvfp4_amax_noalloc: the amax pass with the library's per-GPU scratch array
+    instead of a workspace (calls that overlap on one GPU race)."""
+    rows, cols = _input2d(x)
+    cfg = make_config(rht=rht, rht_mask=rht_mask)
+    if out is not None:
+        _tensor(out, "out", torch.float32, min_numel=1)
+    dev = _same_gpu(x, out=out)
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=dev)
+    st = lib().nvfp4_amax_noalloc(_ptr(x), _dtype_code(x), rows, cols, ctypes.byref(cfg), _ptr(out),
+                                  _stream(dev, stream))
+    _check(st, "nvfp4_amax_noalloc")
     return out
 
 

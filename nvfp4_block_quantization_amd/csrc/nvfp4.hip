@@ -29,6 +29,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "nvfp4.h"
@@ -818,6 +819,48 @@ using namespace nvfp4;
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// ---- the amax pass without a caller workspace ---------------------------------
+// For callers that cannot allocate device memory (graph capture, serving loops):
+// the pass's per-workgroup partial maxima go to this file-scope array instead of
+// a workspace.  Each GPU the library runs on holds its own copy (4 KB) until the
+// process ends.  In host code `scratch` only names the symbol: its device
+// address, different on every GPU, comes from hipGetSymbolAddress with that GPU
+// current, once per device, and only that address is passed to kernels.  Every
+// call on one GPU uses the same array, so calls that overlap on one GPU (on
+// different streams, or from different threads) race; the partial kernel
+// overwrites every entry the finish kernel reads, so nothing needs clearing.
+constexpr int kScratchFloats = kAmaxMaxParts;
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mutex;
+static float* g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the GPU that runs `s` (the current device
+// for the null stream).
+static nvfp4_status scratch_for_stream(hipStream_t s, float** out) {
+  int dev = 0;
+  if (s) {
+    if (hipStreamGetDevice(s, &dev) != hipSuccess) return NVFP4_ERR_HIP;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return NVFP4_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return NVFP4_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return NVFP4_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return NVFP4_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p) return NVFP4_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return NVFP4_OK;
+}
+
 // The value a C caller passed for an enum-typed parameter, read from its bytes:
 // a value outside the enumerators is legal in C but may not be loaded as the
 // C++ enum type, and validation must see it to reject it.
@@ -889,23 +932,24 @@ size_t nvfp4_amax_workspace_bytes(int64_t rows, int64_t cols) {
   return sizeof(float) * (size_t)amax_parts(rows, cols);
 }
 
-nvfp4_status nvfp4_amax(const void* x, nvfp4_dtype dtype_arg, int64_t rows, int64_t cols, const nvfp4_config* cfg,
-                        float* amax_dev, void* workspace, size_t workspace_bytes, void* stream) {
+// Argument checks shared by both amax entry points.
+static nvfp4_status amax_args(const void* x, int dtype, int64_t rows, int64_t cols, bool rht, const float* amax_dev) {
   if (!dims_ok(rows, cols)) return NVFP4_ERR_SHAPE;
-  const int dtype = enum_bits(dtype_arg);
   if (dtype != NVFP4_IN_BF16 && dtype != NVFP4_IN_F32) return NVFP4_ERR_DTYPE;
-  const bool rht = cfg && cfg->rht;
   if (rht && cols % 16) return NVFP4_ERR_SHAPE;
   if (!amax_dev) return NVFP4_ERR_NULL;
   const int64_t n = rows * cols;
   if (n > 0 && !x) return NVFP4_ERR_NULL;
   if (n > 0 && !aligned16(x)) return NVFP4_ERR_ALIGN;
-  const int parts = amax_parts(rows, cols);
-  if (!workspace || workspace_bytes < sizeof(float) * (size_t)parts) return NVFP4_ERR_WORKSPACE;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  float* partials = reinterpret_cast<float*>(workspace);
+  return NVFP4_OK;
+}
+
+// The two amax kernels: partial maxima of `parts` workgroups into `partials`,
+// then their maximum into amax_dev.
+static nvfp4_status launch_amax(const void* x, int dtype, int64_t rows, int64_t cols, bool rht, uint32_t mask,
+                                float* amax_dev, float* partials, int parts, hipStream_t s) {
+  const int64_t n = rows * cols;
   if (n > 0) {
-    const uint32_t mask = rht ? cfg->rht_sign_mask : 0u;
     with_dtype(dtype, [&](auto DT) {
       with_bool(rht, [&](auto RHT) {
         hipLaunchKernelGGL((amax_partial_kernel<DT(), RHT()>), dim3(parts), dim3(kThreads), 0, s, x, n, mask,
@@ -917,6 +961,33 @@ nvfp4_status nvfp4_amax(const void* x, nvfp4_dtype dtype_arg, int64_t rows, int6
     hipLaunchKernelGGL(amax_finish_kernel, dim3(1), dim3(kThreads), 0, s, partials, 0, amax_dev);
   }
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+nvfp4_status nvfp4_amax(const void* x, nvfp4_dtype dtype_arg, int64_t rows, int64_t cols, const nvfp4_config* cfg,
+                        float* amax_dev, void* workspace, size_t workspace_bytes, void* stream) {
+  const int dtype = enum_bits(dtype_arg);
+  const bool rht = cfg && cfg->rht;
+  const nvfp4_status st = amax_args(x, dtype, rows, cols, rht, amax_dev);
+  if (st != NVFP4_OK) return st;
+  const int parts = amax_parts(rows, cols);
+  if (!workspace || workspace_bytes < sizeof(float) * (size_t)parts) return NVFP4_ERR_WORKSPACE;
+  return launch_amax(x, dtype, rows, cols, rht, rht ? cfg->rht_sign_mask : 0u, amax_dev,
+                     reinterpret_cast<float*>(workspace), parts, reinterpret_cast<hipStream_t>(stream));
+}
+
+nvfp4_status nvfp4_amax_noalloc(const void* x, nvfp4_dtype dtype_arg, int64_t rows, int64_t cols,
+                                const nvfp4_config* cfg, float* amax_dev, void* stream) {
+  const int dtype = enum_bits(dtype_arg);
+  const bool rht = cfg && cfg->rht;
+  const nvfp4_status st = amax_args(x, dtype, rows, cols, rht, amax_dev);
+  if (st != NVFP4_OK) return st;
+  const int parts = amax_parts(rows, cols);
+  if (parts > kScratchFloats) return NVFP4_ERR_WORKSPACE;  // never for the capped partial count
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  float* partials = nullptr;
+  const nvfp4_status sp = scratch_for_stream(s, &partials);
+  if (sp != NVFP4_OK) return sp;
+  return launch_amax(x, dtype, rows, cols, rht, rht ? cfg->rht_sign_mask : 0u, amax_dev, partials, parts, s);
 }
 
 nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dtype_arg, int64_t rows, int64_t cols, const nvfp4_config* cfg,

@@ -257,3 +257,17 @@ def test_binding_mxfp4_and_gemm_checks():
         nv.mxfp4_gemm(_t(64, 64), _t(64, 8), _t(32, 64), _t(32, 4))
     with pytest.raises(TypeError, match="GPU"):
         nv.mxfp4_gemm(_t(64, 64), _t(64, 4), _t(32, 64), _t(32, 4))
+
+
+def test_amax_noalloc_validation():
+    """The allocation-free amax rejects bad arguments on the host, before it
+    looks up its per-GPU scratch array or launches anything."""
+    L = nv.lib()
+    P = ctypes.c_void_p
+    cfg = nv.make_config(rht=True)
+    assert L.nvfp4_amax_noalloc(P(FAKE), 0, 64, 24, ctypes.byref(cfg), P(FAKE), None) == nv.ERR_SHAPE
+    assert L.nvfp4_amax_noalloc(P(FAKE), 0, -1, 64, None, P(FAKE), None) == nv.ERR_SHAPE
+    assert L.nvfp4_amax_noalloc(P(FAKE), 0, 64, 64, None, None, None) == nv.ERR_NULL
+    assert L.nvfp4_amax_noalloc(None, 0, 64, 64, None, P(FAKE), None) == nv.ERR_NULL
+    assert L.nvfp4_amax_noalloc(P(FAKE + 4), 0, 64, 64, None, P(FAKE), None) == nv.ERR_ALIGN
+    assert L.nvfp4_amax_noalloc(P(FAKE), 7, 64, 64, None, P(FAKE), None) == nv.ERR_DTYPE
