@@ -301,6 +301,9 @@ struct RowChunk {
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{cc.lo, cc.hi}, rc, 8u * lb, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b8((uint8_t)code, rsc, (lb & 1) == 0 ? (lb >> 1) : kDrop, 0, 0);
       } else {
+        // exact 4/6 errors for every block: the estimate path (used by the strip
+        // kernel) holds more registers live, which costs this kernel a wave per
+        // SIMD and measured slower on the 1x16 activation and gradient shapes
         const BlockResult r = quant_block16<SR, RULE>(y, w, tab, ts.den6, ts.den4);
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{r.codes.lo, r.codes.hi}, rc, 8u * lb, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b8((uint8_t)r.sb, rsc, lb, 0, 0);
@@ -486,9 +489,9 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
       res.sb = mx_scale_code(m);
       res.codes = mx_round16<SR>(y, res.sb, w);
     } else if constexpr (TWO_D) {
-      res = quant_tile_row16<SR, RULE>(y, w, tab, ts.den6, ts.den4);
+      res = quant_tile_row16<SR, RULE, true>(y, w, tab, ts.den6, ts.den4);
     } else {
-      res = quant_block16<SR, RULE>(y, w, tab, ts.den6, ts.den4);
+      res = quant_block16<SR, RULE, true>(y, w, tab, ts.den6, ts.den4);
     }
 
     {
@@ -587,7 +590,7 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
       }
       sbc = res.sb;
     } else {
-      const BlockResult rc = quant_block16<SR, RULE>(y, w, tab, ts.den6, ts.den4);
+      const BlockResult rc = quant_block16<SR, RULE, true>(y, w, tab, ts.den6, ts.den4);
       cc = rc.codes;
       sbc = rc.sb;
     }

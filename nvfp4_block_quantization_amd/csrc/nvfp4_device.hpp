@@ -467,12 +467,14 @@ struct Divisor {
   float den;   // fl(T * S_t)
   float y;     // fl(1 / den)
   bool fast;   // den within the range where the corrected product is exact
+  bool est;    // den within the range where the 4/6 error estimates are bounded
 };
 
 __device__ __forceinline__ Divisor make_divisor(float den) {
   Divisor d;
   d.den = den;
   d.fast = den >= 0x1p-100f && den <= 0x1p100f;
+  d.est = den >= 0x1p-48f && den <= 0x1p48f;
   d.y = d.fast ? __fdiv_rn(1.0f, den) : 0.0f;
   return d;
 }
@@ -498,6 +500,157 @@ __device__ __forceinline__ Scale block_scale(float m, const Divisor& den, const 
   return s;
 }
 
+// ------------------------------------------------- 4/6 error estimates ---
+//
+// The 4/6 choice compares the candidates' errors E_T: a binary32 reduction
+// (pairwise sum, or max) of per-element terms of eps = fl(y - fl(v * d)).
+// Most blocks are decided without forming those terms.  While an element is
+// rounded, its residual in the scaled domain, r = fl(z - v) with z = fl(y * e),
+// is accumulated (|r|, r^2 or max |r|), and d (MSE: d^2) times the result
+// estimates E_T.  To first order in u = 2^-24, for a block of n values with
+// max m, both the estimate and E_T lie within
+//   MAE:    3u n m + 21u E         MSE: 6u sum|y||t| + 26u E
+//   MAXERR: 3u m + 4u E
+// of the exact-arithmetic error (t = y - v d; sum|y||t| <= (n m^2/16 + 16 E)/2
+// by the arithmetic-geometric mean), provided the tensor scale keeps every
+// non-zero d within [2^-60, 2^60] (den within [2^-48, 2^48]) and d > 0.  The
+// bounds applied below are at least 2.5 times these.  When the estimates
+// differ by more than the sum of the two candidates' bounds, their order is
+// the order of the exact errors and decides the block; otherwise (near-ties,
+// zero or extreme scales, non-finite values) the exact errors are formed.
+template <int RULE>
+__device__ __forceinline__ float residual_first(float r) {
+  if constexpr (RULE == kRuleMse) {
+    return r * r;
+  } else {
+    return fabsf(r);
+  }
+}
+
+template <int RULE>
+__device__ __forceinline__ float residual_acc(float acc, float r) {
+  if constexpr (RULE == kRuleMse) {
+    return __builtin_fmaf(r, r, acc);
+  } else if constexpr (RULE == kRuleMaxErr) {
+    return fmaxf(acc, fabsf(r));
+  } else {
+    return acc + fabsf(r);
+  }
+}
+
+template <int RULE>
+__device__ __forceinline__ float residual_join(float a, float b) {
+  if constexpr (RULE == kRuleMaxErr) {
+    return fmaxf(a, b);
+  } else {
+    return a + b;
+  }
+}
+
+template <int RULE>
+__device__ __forceinline__ float residual_join4(const float* a) {
+  return residual_join<RULE>(residual_join<RULE>(a[0], a[1]), residual_join<RULE>(a[2], a[3]));
+}
+
+// Stochastic rounding of 16 values under both candidates (as sr_pair_regs),
+// with each convert's two codes decoded at once to accumulate the residual
+// sums of the scale-to-6 (s6) and scale-to-4 (s4) candidates.
+template <int SEL, int RULE>
+__device__ __forceinline__ void sr_pair_step(const float* y, float e6, float e4, const uint32_t* w, uint32_t* P,
+                                             float* a6, float* a4) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int k = (r >> 1) * 8 + (r & 1) + 2 * SEL;
+    const f32x2 z = {y[k] * e6, y[k] * e4};
+    if constexpr (SEL == 0) {
+      P[r] = cvt_sr_byte0_fresh(z, w[k]);
+    } else {
+      P[r] = cvt_sr_byte<SEL>(P[r], z, w[k]);
+    }
+    const f32x2 v = fp4_pair_values<SEL>(P[r]);
+    if constexpr (SEL == 0) {
+      a6[r] = residual_first<RULE>(z.x - v.x);
+      a4[r] = residual_first<RULE>(z.y - v.y);
+    } else {
+      a6[r] = residual_acc<RULE>(a6[r], z.x - v.x);
+      a4[r] = residual_acc<RULE>(a4[r], z.y - v.y);
+    }
+  }
+}
+
+template <int RULE>
+__device__ __forceinline__ void sr_pair_sums(const float* y, float e6, float e4, const uint32_t* w, uint32_t* P,
+                                             float& s6, float& s4) {
+  float a6[4], a4[4];
+  sr_pair_step<0, RULE>(y, e6, e4, w, P, a6, a4);
+  sr_pair_step<1, RULE>(y, e6, e4, w, P, a6, a4);
+  sr_pair_step<2, RULE>(y, e6, e4, w, P, a6, a4);
+  sr_pair_step<3, RULE>(y, e6, e4, w, P, a6, a4);
+  s6 = residual_join4<RULE>(a6);
+  s4 = residual_join4<RULE>(a4);
+}
+
+// Round-to-nearest-even of 16 values with reciprocal e (the codes of
+// round16<false>) and the candidate's residual sum s.
+template <int SEL, int RULE>
+__device__ __forceinline__ void rne_pair_step(const float* y, float e, uint32_t& lo, uint32_t& hi, float* a) {
+  const float z0 = y[2 * SEL] * e, z1 = y[2 * SEL + 1] * e;
+  const float z8 = y[8 + 2 * SEL] * e, z9 = y[9 + 2 * SEL] * e;
+  if constexpr (SEL == 0) {
+    lo = cvt_rne_byte0_fresh(z0, z1);
+    hi = cvt_rne_byte0_fresh(z8, z9);
+  } else {
+    lo = cvt_rne_pair<SEL>(lo, z0, z1);
+    hi = cvt_rne_pair<SEL>(hi, z8, z9);
+  }
+  const f32x2 vl = fp4_pair_values<SEL>(lo), vh = fp4_pair_values<SEL>(hi);
+  constexpr int c = 2 * (SEL & 1);  // chains 0, 1 take bytes 0 and 2; chains 2, 3 bytes 1 and 3
+  if constexpr (SEL < 2) {
+    a[c] = residual_first<RULE>(z0 - vl.x);
+    a[c + 1] = residual_first<RULE>(z8 - vh.x);
+  } else {
+    a[c] = residual_acc<RULE>(a[c], z0 - vl.x);
+    a[c + 1] = residual_acc<RULE>(a[c + 1], z8 - vh.x);
+  }
+  a[c] = residual_acc<RULE>(a[c], z1 - vl.y);
+  a[c + 1] = residual_acc<RULE>(a[c + 1], z9 - vh.y);
+}
+
+template <int RULE>
+__device__ __forceinline__ BlockCodes round16_sums(const float* y, float e, float& s) {
+  uint32_t lo, hi;
+  float a[4];
+  rne_pair_step<0, RULE>(y, e, lo, hi, a);
+  rne_pair_step<1, RULE>(y, e, lo, hi, a);
+  rne_pair_step<2, RULE>(y, e, lo, hi, a);
+  rne_pair_step<3, RULE>(y, e, lo, hi, a);
+  s = residual_join4<RULE>(a);
+  return BlockCodes{lo, hi};
+}
+
+template <int RULE>
+__device__ __forceinline__ float error_estimate(float s, float d) {
+  if constexpr (RULE == kRuleMse) {
+    return d * (d * s);
+  } else {
+    return d * s;
+  }
+}
+
+// Whether the estimates a6, a4 of a block of N values with max m decide it.
+template <int RULE, int N>
+__device__ __forceinline__ bool estimates_decide(float a6, float a4, float m) {
+  float b;
+  if constexpr (RULE == kRuleMae) {
+    b = 0x1p-18f * (a6 + a4) + (0x1p-20f * N) * m;
+  } else if constexpr (RULE == kRuleMaxErr) {
+    b = 0x1p-19f * (a6 + a4) + 0x1p-20f * m;
+  } else {
+    b = 0x1p-16f * (a6 + a4) + (0x1p-23f * N) * (m * m);
+  }
+  return fabsf(a4 - a6) > b;
+}
+
 struct BlockResult {
   BlockCodes codes;
   uint32_t sb;
@@ -510,7 +663,8 @@ struct BlockResult {
 // candidate is formed; its stochastic rounding pairs consecutive elements in
 // one convert, so the odd elements' words are shifted right by one (the
 // convert's second slot reads its word one bit lower).
-template <bool SR, int RULE, bool TILE = false>
+// EST: decide by the error estimates where they suffice (the exact errors otherwise).
+template <bool SR, int RULE, bool TILE = false, bool EST = false>
 __device__ __forceinline__ BlockResult choose16(const float* y, float m, const uint32_t* w, const f32x2* tab,
                                                 const Divisor& den6, const Divisor& den4) {
   const Scale s6 = block_scale(m, den6, tab);
@@ -524,55 +678,87 @@ __device__ __forceinline__ BlockResult choose16(const float* y, float m, const u
   } else {
     const Scale s4 = block_scale(m, den4, tab);
     BlockCodes c6, c4;
-    if constexpr (SR) {
-      const CodePair cp = round16_sr_both(y, s6.e, s4.e, w);
-      c6 = cp.c6;
-      c4 = cp.c4;
-    } else {
-      c6 = round16<false>(y, s6.e, nullptr);
-      c4 = round16<false>(y, s4.e, nullptr);
-    }
-    float t[16];
-    error_terms16<RULE>(y, c6, s6.d, t);
-    float err6 = reduce16<RULE>(t);
-    error_terms16<RULE>(y, c4, s4.d, t);
-    float err4 = reduce16<RULE>(t);
-    if constexpr (TILE) {
-      if constexpr (RULE == kRuleMaxErr) {
-        err6 = row16_max(err6);
-        err4 = row16_max(err4);
+    bool decided = false, pick4 = false;
+    if constexpr (EST) {
+      float f6, f4;  // residual sums in the scaled domain
+      if constexpr (SR) {
+        uint32_t P[4];
+        sr_pair_sums<RULE>(y, s6.e, s4.e, w, P, f6, f4);
+        c6.lo = nibble_merge(P[0], P[1] << 4);
+        c6.hi = nibble_merge(P[2], P[3] << 4);
+        c4.lo = nibble_merge(P[0] >> 4, P[1]);
+        c4.hi = nibble_merge(P[2] >> 4, P[3]);
       } else {
-        err6 = row16_pairwise_sum(err6);
-        err4 = row16_pairwise_sum(err4);
+        c6 = round16_sums<RULE>(y, s6.e, f6);
+        c4 = round16_sums<RULE>(y, s4.e, f4);
+      }
+      if constexpr (TILE) {
+        if constexpr (RULE == kRuleMaxErr) {
+          f6 = row16_max(f6);
+          f4 = row16_max(f4);
+        } else {
+          f6 = row16_pairwise_sum(f6);
+          f4 = row16_pairwise_sum(f4);
+        }
+      }
+      const float a6 = error_estimate<RULE>(f6, s6.d), a4 = error_estimate<RULE>(f4, s4.d);
+      // (evaluated in full, so that the sums are formed while the codes are)
+      decided = den6.est & (s6.d > 0.0f) & estimates_decide<RULE, TILE ? 256 : 16>(a6, a4, m);
+      pick4 = a4 < a6;
+    } else {
+      if constexpr (SR) {
+        const CodePair cp = round16_sr_both(y, s6.e, s4.e, w);
+        c6 = cp.c6;
+        c4 = cp.c4;
+      } else {
+        c6 = round16<false>(y, s6.e, nullptr);
+        c4 = round16<false>(y, s4.e, nullptr);
       }
     }
-    const bool pick4 = err4 < err6;  // a tie keeps the scale-to-6 block
+    if (!decided) {
+      // the exact errors (in a 16x16 tile every lane of the row takes this branch together)
+      float t[16];
+      error_terms16<RULE>(y, c6, s6.d, t);
+      float err6 = reduce16<RULE>(t);
+      error_terms16<RULE>(y, c4, s4.d, t);
+      float err4 = reduce16<RULE>(t);
+      if constexpr (TILE) {
+        if constexpr (RULE == kRuleMaxErr) {
+          err6 = row16_max(err6);
+          err4 = row16_max(err4);
+        } else {
+          err6 = row16_pairwise_sum(err6);
+          err4 = row16_pairwise_sum(err4);
+        }
+      }
+      pick4 = err4 < err6;  // a tie keeps the scale-to-6 block
+    }
     return pick4 ? BlockResult{c4, s4.sb, s4.e, 1u} : BlockResult{c6, s6.sb, s6.e, 0u};
   }
 }
 
 // One 16-element block held by one lane.  den6: fl(6 * S_t), den4: fl(4 * S_t).
-template <bool SR, int RULE>
+template <bool SR, int RULE, bool EST = false>
 __device__ __forceinline__ BlockResult quant_block16(const float* y, const uint32_t* w, const f32x2* tab,
                                                      const Divisor& den6, const Divisor& den4) {
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(y[i]));
-  return choose16<SR, RULE>(y, m, w, tab, den6, den4);
+  return choose16<SR, RULE, false, EST>(y, m, w, tab, den6, den4);
 }
 
 // A 16x16 tile spread over the 16 lanes of a DPP row, one tile row per lane.
 // The tile max and the candidates' errors are reduced across the row; the
 // error tree over the 256 values in row-major order is the in-lane pairwise
 // sum of each row followed by pairwise sums across lanes.
-template <bool SR, int RULE>
+template <bool SR, int RULE, bool EST = false>
 __device__ __forceinline__ BlockResult quant_tile_row16(const float* y, const uint32_t* w, const f32x2* tab,
                                                         const Divisor& den6, const Divisor& den4) {
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(y[i]));
   m = row16_max(m);
-  return choose16<SR, RULE, true>(y, m, w, tab, den6, den4);
+  return choose16<SR, RULE, true, EST>(y, m, w, tab, den6, den4);
 }
 
 // ----------------------------------------------------------------- MXFP4 ---

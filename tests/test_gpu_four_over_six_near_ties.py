@@ -1,0 +1,97 @@
+"""4/6 blocks whose two candidates have (nearly) equal errors.
+
+The strip kernel (column copies, 16x16 tiles) decides most 4/6 blocks from
+error estimates formed in the scaled domain and computes the exact binary32
+errors only where the two estimates are within their rounding bound of each
+other, or where a scale is zero.  These inputs put many blocks in that band:
+constant tiles and single-spike tiles whose two candidate scales are both
+exact E4M3 values, so that both candidates' errors are rounding noise, plus
+all-zero blocks (tied at zero).  The CPU test shows, with the oracle alone,
+that the input really holds such near-ties; the GPU tests require every output
+byte to equal the oracle's.
+"""
+import numpy as np
+import pytest
+
+import oracle
+
+RULES = ("mse", "mae", "maxerr")
+
+# E4M3 values k with 1.5 k also an E4M3 value: a block max of k / 256 (amax 1,
+# cap 256) gives the scale-to-6 factor k and the scale-to-4 factor 1.5 k.
+TIE_FACTORS = (0.25, 0.5, 1.0, 1.25, 2.0, 2.5, 4.0, 8.0, 10.0, 16.0, 32.0, 64.0)
+
+
+def near_tie_input(rows: int = 256, cols: int = 256, seed: int = 3) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    x = np.zeros((rows, cols), np.float32)
+    for ti in range(rows // 16):
+        for tj in range(cols // 16):
+            t = x[16 * ti:16 * ti + 16, 16 * tj:16 * tj + 16]
+            fam = (ti * 7 + tj * 3) % 5
+            c = np.float32(TIE_FACTORS[(ti + tj) % len(TIE_FACTORS)] / 256.0)
+            if fam == 0:  # constant tile
+                t[:] = c
+            elif fam == 1:  # one spike per tile, the rest zero
+                t[rng.integers(16), rng.integers(16)] = c
+            elif fam == 2:  # one spike per row, alternating signs
+                for r in range(16):
+                    t[r, rng.integers(16)] = c if r % 2 == 0 else -c
+            elif fam == 3:  # all zero
+                pass
+            else:  # ordinary values around the same scale
+                t[:] = (rng.standard_normal((16, 16)) * c / 3.0).astype(np.float32)
+    x[0, 0] = 1.0  # the tensor amax
+    return x
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    # truncation: exact for the constant and spike values (at most 8
+    # significant bits); the ordinary values just become other bf16 values
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_input_has_near_ties():
+    """Without any GPU: a good share of the 1x16 row blocks have candidate
+    errors within 2^-16 of each other (relative), some exactly equal."""
+    x = near_tie_input()
+    s_t = oracle.tensor_scale(oracle.amax(x), 256.0)
+    for rule in RULES:
+        close = tied = total = 0
+        for r in range(0, x.shape[0], 5):
+            for b in range(x.shape[1] // 16):
+                y = x[r, 16 * b:16 * b + 16]
+                if not np.any(y):
+                    continue
+                _, _, _, (e6, e4) = oracle.quantize_block(y, s_t, rule)
+                total += 1
+                tied += e6 == e4
+                close += abs(e6 - e4) <= 2.0 ** -16 * max(e6, e4)
+        assert close >= total // 4, (rule, close, total)
+        assert tied >= 1, (rule, tied, total)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("block", ["1d", "2d"])
+@pytest.mark.parametrize("sr", [False, True])
+@pytest.mark.parametrize("rule", RULES)
+def test_near_ties_bit_exact(rule, sr, block, dtype):
+    torch = pytest.importorskip("torch")
+    nv = pytest.importorskip("nvfp4_block_quantization_amd")
+    x = near_tie_input()
+    xin = x if dtype == "f32" else bf16_bits(x)
+    print(f"[near-ties] rule={rule} sr={sr} block={block} dtype={dtype}", flush=True)
+    t = torch.from_numpy(xin)
+    xg = (t.view(torch.bfloat16) if dtype == "bf16" else t).cuda()
+    amax_t = nv.amax(xg)
+    out = nv.quantize(xg, amax_t, block=block, rowwise=True, colwise=True, sr=sr, sr_seed=11, rule=rule,
+                      scale_cap=256.0)
+    torch.cuda.synchronize()
+    a = oracle.amax(xin)
+    ref = oracle.quantize(xin, oracle.make_config(block=block, emit_row=True, emit_col=True, sr=sr, sr_seed=11,
+                                                  rule=rule, cap=256.0), a)
+    for k in ("codes_row", "scales_row", "codes_col", "scales_col"):
+        got = out[k].cpu().numpy()
+        bad = np.argwhere(got != ref[k])
+        assert bad.size == 0, f"{k} differs at {len(bad)} places, first {bad[:5].tolist()}"
