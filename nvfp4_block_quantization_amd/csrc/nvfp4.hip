@@ -535,9 +535,10 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
         for (int j = 0; j < 4; ++j) dv[j] = make_float4(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]);
       }
       if constexpr (SR) {
-        // one 4-byte store per word: the Philox results sit in scattered
-        // registers, and 16-byte stores would first gather them with moves
-        typedef __attribute__((address_space(3))) volatile uint32_t lds_word;
+        // 4-byte words, which the compiler pairs into two-address stores
+        // (ds_write2_b32 takes its two words from any two registers; 16-byte
+        // stores would first gather the scattered Philox results with moves)
+        typedef __attribute__((address_space(3))) uint32_t lds_word;
         lds_word* dw = (lds_word*)(lds_w + row * WP + 16 * bj);
 #pragma unroll
         for (int k = 0; k < 16; ++k) dw[k] = w[k];
