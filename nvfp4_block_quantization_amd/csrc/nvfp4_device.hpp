@@ -509,7 +509,7 @@ __device__ __forceinline__ Scale block_scale(float m, const Divisor& den, const 
 // is accumulated (|r|, r^2 or max |r|), and d (MSE: d^2) times the result
 // estimates E_T.  To first order in u = 2^-24, for a block of n values with
 // max m, both the estimate and E_T lie within
-//   MAE:    3u n m + 21u E         MSE: 6u sum|y||t| + 26u E
+//   MAE:    3u n m + 21u E         MSE: 6u sum|y||t| + 27u E
 //   MAXERR: 3u m + 4u E
 // of the exact-arithmetic error (t = y - v d; sum|y||t| <= (n m^2/16 + 16 E)/2
 // by the arithmetic-geometric mean), provided the tensor scale keeps every
