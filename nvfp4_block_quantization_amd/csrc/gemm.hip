@@ -81,16 +81,18 @@ struct MxStage {
 
 __device__ __forceinline__ int piece_slot(int row, int part) { return row * 4 + (part ^ ((row >> 2) & 3)); }
 
-// Grouped raster: 4 tile rows per group, columns outer, so the workgroups that
-// run together on one XCD share A tiles (4 rows) and B tiles (consecutive columns).
+// Grouped raster: 8 tile columns per group, rows outer, so that the 32
+// workgroups one XCD runs at a time cover 4 tile rows x 8 tile columns and
+// share their A and B slices in its L2 (measured 6% faster on 8192x20480x5120
+// than groups of 4 tile rows).
 __device__ __forceinline__ void grouped_tile(uint32_t L, uint32_t tiles_m, uint32_t tiles_n, uint32_t& tm,
                                              uint32_t& tn) {
-  constexpr uint32_t G = 4;
-  const uint32_t group = L / (G * tiles_n), first = group * G;
-  const uint32_t gsize = tiles_m - first < G ? tiles_m - first : G;
-  const uint32_t in = L - group * G * tiles_n;
-  tm = first + in % gsize;
-  tn = in / gsize;
+  constexpr uint32_t G = 8;
+  const uint32_t group = L / (G * tiles_m), first = group * G;
+  const uint32_t gsize = tiles_n - first < G ? tiles_n - first : G;
+  const uint32_t in = L - group * G * tiles_m;
+  tn = first + in % gsize;
+  tm = in / gsize;
 }
 
 template <int C>
@@ -178,18 +180,28 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_dma_kernel(const uint8_t* __
 
   const int wr = 128 * (wave >> 1), wc = 128 * (wave & 1);  // this wave's quarter of the tile
   const int64_t nsteps = K / kStepK, last = nsteps - 1;
-  // 10 loads per step and thread; past the last step they re-read the last step
-  auto issue = [&](int64_t step) {
+  // 10 loads per step and thread (q = 0 .. 9: A and B pieces j = q / 2
+  // alternately, then the two scale words); past the last step they re-read it
+  auto issue_one = [&](int64_t step, int q) {
     const int64_t st_ = step < last ? step : last;
     MxStage& d = st[step & (kRing - 1)];
     const int64_t kb = st_ * (kStepK / 2);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      __builtin_amdgcn_global_load_lds(A + offa[j] + kb, &d.a[256 * j + wbase], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(B + offb[j] + kb, &d.b[256 * j + wbase], 16, 0, 0);
+    if (q < 8) {
+      const int j = q >> 1;
+      if ((q & 1) == 0) {
+        __builtin_amdgcn_global_load_lds(A + offa[j] + kb, &d.a[256 * j + wbase], 16, 0, 0);
+      } else {
+        __builtin_amdgcn_global_load_lds(B + offb[j] + kb, &d.b[256 * j + wbase], 16, 0, 0);
+      }
+    } else if (q == 8) {
+      __builtin_amdgcn_global_load_lds(gsa + st_ * (kStepK / 32), &d.sa[wbase], 4, 0, 0);
+    } else {
+      __builtin_amdgcn_global_load_lds(gsb + st_ * (kStepK / 32), &d.sb[wbase], 4, 0, 0);
     }
-    __builtin_amdgcn_global_load_lds(gsa + st_ * (kStepK / 32), &d.sa[wbase], 4, 0, 0);
-    __builtin_amdgcn_global_load_lds(gsb + st_ * (kStepK / 32), &d.sb[wbase], 4, 0, 0);
+  };
+  auto issue = [&](int64_t step) {
+#pragma unroll
+    for (int q = 0; q < 10; ++q) issue_one(step, q);
   };
   issue(0);
   issue(1);
@@ -206,9 +218,16 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_dma_kernel(const uint8_t* __
     const MxStage& nxt = st[(s + 1) & (kRing - 1)];
     mx_read<1>(cur, wr, wc, l, h, f1a, f1b);
     __builtin_amdgcn_sched_barrier(0);
-    mx_mma<0>(f0a, f0b, sa, sb, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(s + 3);          // into stage (s + 3) % 4 = (s - 1) % 4, read by every wave before the last barrier
+    // the chunk-0 products, with the loads of step s + 3 (into stage (s + 3) % 4 =
+    // (s - 1) % 4, read by every wave before the last barrier) issued between them
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[i][j] = mx_mfma_s<0>(f0a[i], f0b[j], sa[i], sb[j], acc[i][j]);
+        if (4 * i + j < 10) issue_one(s + 3, 4 * i + j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     MX_WAIT_VM_LGKM0(20);  // this thread's loads of step s + 1 have landed; steps s + 2, s + 3 pending
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
