@@ -210,7 +210,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // of 16-element blocks.  One block per lane; a chunk is U blocks per lane with
 // each wave instruction loading 64 consecutive blocks.  Persistent workgroups
 // walk the chunks and prefetch the next chunk's input while quantizing the
-// current one (ping-pong register buffers).  Loads and stores go through
+// current one (ping-pong register buffers); a grid of one workgroup per chunk
+// runs the same kernel once through.  Loads and stores go through
 // buffer resources that end where the chunk's blocks end, so no lane branches
 // around a memory access and every wait for a prefetched chunk is exact.
 template <int DT>
@@ -323,12 +324,18 @@ __global__ __launch_bounds__(kThreads) void quant_row_kernel(const void* __restr
   const int64_t G = gridDim.x;
   const PhiloxKey key = philox_key(p.k0, p.k1);
   RowChunk<DT, RHT, SR, RULE, U, MX> A, B;
-  // Branch-free trips: chunks past the end load zeros and store nothing.
   int64_t c = blockIdx.x;
   A.load(x, c, nblocks);
+  if (G >= nchunks) {  // one chunk per workgroup
+    A.process(c, nblocks, p, tab, ts, key);
+    return;
+  }
+  // Branch-free trips: chunks past the end load zeros and store nothing; the
+  // loop leaves (uniformly) rather than quantize a chunk that does not exist.
   for (; c < nchunks; c += 2 * G) {
     B.load(x, c + G, nblocks);
     A.process(c, nblocks, p, tab, ts, key);
+    if (c + G >= nchunks) break;
     A.load(x, c + 2 * G, nblocks);
     B.process(c + G, nblocks, p, tab, ts, key);
   }
@@ -1108,7 +1115,13 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dtype_arg, int64_t rows, 
         with_bool(cfg->sr != 0, [&](auto SR) {
           with_rule(cfg->rule, [&](auto RULE) {
             auto k = quant_row_kernel<DT(), RHT(), SR(), RULE(), kRowU, false>;
-            int64_t grid = resident_grid(k);
+            // With stochastic rounding a chunk's arithmetic (a Philox word per
+            // element) is long enough for the other resident waves to hide a new
+            // workgroup's first load, and one workgroup per chunk lets the
+            // dispatcher balance the chunks over the CUs (a persistent grid gives
+            // some workgroups one chunk more than others).  Lighter chunks keep
+            // the persistent grid, whose prefetch hides the load latency.
+            int64_t grid = SR() ? nchunks : resident_grid(k);
             if (grid > nchunks) grid = nchunks;
             hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), 0, s, x, nblocks, p);
           });
