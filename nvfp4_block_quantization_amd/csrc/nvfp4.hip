@@ -727,17 +727,33 @@ __global__ void tensor_scale_kernel(const float* __restrict__ amax, float cap6, 
 // v* = nearest-even E2M1 of T|y| / m, taken by comparing T|y| with the
 // midpoints times m (exact products), xh* = fl64(v* * m / T).
 constexpr int kMaxBins = 64;
+// The workgroup's histogram is kept in 16 copies, lane i of every DPP row
+// adding into copy i: lanes of one wave that hit the same bin then collide in
+// groups of at most four instead of sixty-four (LDS atomics to one address
+// serialize).  The copies are summed when the workgroup ends.
+constexpr int kHistCopies = 16;
 
-__device__ __forceinline__ double exact_scale_value(double ty, double m, const double* xs) {
-  // midpoints of the E2M1 grid; ties go to the even grid index
-  if (ty <= 0.25 * m) return 0.0;
-  if (ty < 0.75 * m) return xs[1];
-  if (ty <= 1.25 * m) return xs[2];
-  if (ty < 1.75 * m) return xs[3];
-  if (ty <= 2.5 * m) return xs[4];
-  if (ty < 3.5 * m) return xs[5];
-  if (ty <= 5.0 * m) return xs[6];
-  return xs[7];
+// The E2M1 grid values times m / T (binary64), as seven scalars passed by
+// value so that the compiler keeps them in registers: a select between
+// elements of an array (or of a struct behind a reference) becomes a load of
+// the selected element from scratch memory.
+struct ScaledGrid {
+  double x1, x2, x3, x4, x5, x6, x7;
+};
+
+// Midpoints of the E2M1 grid (times m), ties to the even grid index: the first
+// test that holds, in increasing order, picks the value (x7 when none does, as
+// for a NaN).  Written as selects from the top down, so that no lane branches.
+__device__ __forceinline__ double exact_scale_value(double ty, double m, ScaledGrid g) {
+  double v = g.x7;
+  v = ty <= 5.0 * m ? g.x6 : v;
+  v = ty < 3.5 * m ? g.x5 : v;
+  v = ty <= 2.5 * m ? g.x4 : v;
+  v = ty < 1.75 * m ? g.x3 : v;
+  v = ty <= 1.25 * m ? g.x2 : v;
+  v = ty < 0.75 * m ? g.x1 : v;
+  v = ty <= 0.25 * m ? 0.0 : v;
+  return v;
 }
 
 template <int DT, bool RHT, bool TWO_D, int RULE>
@@ -745,10 +761,11 @@ __global__ __launch_bounds__(kThreads) void err_stats_kernel(const void* __restr
                                                              QuantParams p, float inv_w, int nbins,
                                                              double* __restrict__ stats) {
   __shared__ f32x2 tab[128];
-  __shared__ double hist[3 * kMaxBins];
-  for (int k = threadIdx.x; k < 3 * nbins; k += kThreads) hist[k] = 0.0;
+  __shared__ double hist[3 * kMaxBins * kHistCopies];  // [quantity, bin][copy]
+  for (int k = threadIdx.x; k < 3 * nbins * kHistCopies; k += kThreads) hist[k] = 0.0;
   const TensorScale ts = workgroup_setup(p, tab);  // ends with a barrier
   const int g = threadIdx.x >> 4, i = threadIdx.x & 15;
+  double* const mine = hist + i;  // this lane's copy (stride kHistCopies)
   const int64_t rcols = cols / 16, nreg = (rows / 16) * rcols;
   for (int64_t reg0 = (int64_t)blockIdx.x * 16; reg0 < nreg; reg0 += (int64_t)gridDim.x * 16) {
     const int64_t reg = reg0 + g;
@@ -776,10 +793,8 @@ __global__ __launch_bounds__(kThreads) void err_stats_kernel(const void* __restr
     v[6] = fp4_pair_values<2>(res.codes.hi);
     v[7] = fp4_pair_values<3>(res.codes.hi);
     const double T = res.four ? 4.0 : 6.0, md = (double)m;
-    double xs[8];
-    const double grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
-#pragma unroll
-    for (int k = 0; k < 8; ++k) xs[k] = (grid[k] * md) / T;
+    const ScaledGrid xs{(0.5 * md) / T, md / T, (1.5 * md) / T, (2.0 * md) / T,
+                        (3.0 * md) / T, (4.0 * md) / T, (6.0 * md) / T};
     if (!active) continue;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
@@ -791,13 +806,18 @@ __global__ __launch_bounds__(kThreads) void err_stats_kernel(const void* __restr
       const double yd = (double)y[k];
       const double xh = m != 0.0f ? exact_scale_value(T * fabs(yd), md, xs) : 0.0;
       const double es = yd - copysign(xh, yd);
-      atomicAdd(&hist[b], 1.0);
-      atomicAdd(&hist[nbins + b], (double)eps * (double)eps);
-      atomicAdd(&hist[2 * nbins + b], es * es);
+      atomicAdd(&mine[kHistCopies * b], 1.0);
+      atomicAdd(&mine[kHistCopies * (nbins + b)], (double)eps * (double)eps);
+      atomicAdd(&mine[kHistCopies * (2 * nbins + b)], es * es);
     }
   }
   __syncthreads();
-  for (int k = threadIdx.x; k < 3 * nbins; k += kThreads) atomicAdd(&stats[k], hist[k]);
+  for (int k = threadIdx.x; k < 3 * nbins; k += kThreads) {
+    double sum = 0.0;
+#pragma unroll
+    for (int c = 0; c < kHistCopies; ++c) sum += hist[kHistCopies * k + c];
+    atomicAdd(&stats[k], sum);
+  }
 }
 
 __global__ void zero_f64_kernel(double* __restrict__ p, int n) {
