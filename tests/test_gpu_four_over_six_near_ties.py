@@ -1,9 +1,9 @@
 """4/6 blocks whose two candidates have (nearly) equal errors.
 
-The strip kernel (column copies, 16x16 tiles) decides most 4/6 blocks from
-error estimates formed in the scaled domain and computes the exact binary32
-errors only where the two estimates are within their rounding bound of each
-other, or where a scale is zero.  These inputs put many blocks in that band:
+Both quantize kernels decide most 4/6 blocks from error estimates formed in
+the scaled domain and compute the exact binary32 errors only where the two
+estimates are within their rounding bound of each other, or where a scale is
+zero.  These inputs put many blocks in that band:
 constant tiles and single-spike tiles whose two candidate scales are both
 exact E4M3 values, so that both candidates' errors are rounding noise, plus
 all-zero blocks (tied at zero).  The CPU test shows, with the oracle alone,
@@ -73,25 +73,27 @@ def test_input_has_near_ties():
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("block", ["1d", "2d"])
+@pytest.mark.parametrize("block,colwise", [("1d", True), ("2d", True), ("1d", False)])
 @pytest.mark.parametrize("sr", [False, True])
 @pytest.mark.parametrize("rule", RULES)
-def test_near_ties_bit_exact(rule, sr, block, dtype):
+def test_near_ties_bit_exact(rule, sr, block, colwise, dtype):
+    """Row and column copies go through the strip kernel; the 1x16 row copy
+    alone through the row kernel, which decides 4/6 the same way."""
     torch = pytest.importorskip("torch")
     nv = pytest.importorskip("nvfp4_block_quantization_amd")
     x = near_tie_input()
     xin = x if dtype == "f32" else bf16_bits(x)
-    print(f"[near-ties] rule={rule} sr={sr} block={block} dtype={dtype}", flush=True)
+    print(f"[near-ties] rule={rule} sr={sr} block={block} colwise={colwise} dtype={dtype}", flush=True)
     t = torch.from_numpy(xin)
     xg = (t.view(torch.bfloat16) if dtype == "bf16" else t).cuda()
     amax_t = nv.amax(xg)
-    out = nv.quantize(xg, amax_t, block=block, rowwise=True, colwise=True, sr=sr, sr_seed=11, rule=rule,
+    out = nv.quantize(xg, amax_t, block=block, rowwise=True, colwise=colwise, sr=sr, sr_seed=11, rule=rule,
                       scale_cap=256.0)
     torch.cuda.synchronize()
     a = oracle.amax(xin)
-    ref = oracle.quantize(xin, oracle.make_config(block=block, emit_row=True, emit_col=True, sr=sr, sr_seed=11,
+    ref = oracle.quantize(xin, oracle.make_config(block=block, emit_row=True, emit_col=colwise, sr=sr, sr_seed=11,
                                                   rule=rule, cap=256.0), a)
-    for k in ("codes_row", "scales_row", "codes_col", "scales_col"):
+    for k in ("codes_row", "scales_row") + (("codes_col", "scales_col") if colwise else ()):
         got = out[k].cpu().numpy()
         bad = np.argwhere(got != ref[k])
         assert bad.size == 0, f"{k} differs at {len(bad)} places, first {bad[:5].tolist()}"
