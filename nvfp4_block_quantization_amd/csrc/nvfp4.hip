@@ -348,7 +348,8 @@ __global__ __launch_bounds__(kThreads) void quant_row_kernel(const void* __restr
 // 16x16 block g: one block row per lane in the row pass, one block column per
 // lane in the column pass; every LDS exchange of a sub-tile stays inside one
 // wave (wave w owns rows 16w .. 16w + 15 in both passes), so waves run free of
-// each other until the strip's end.  The row copy is stored straight from
+// each other until the strip's end.  16x16 tiles need no column pass: the
+// column copy's codes are the row copy's, transposed across the DPP row.  The row copy is stored straight from
 // registers.  The column copy of a 256-row strip is one full 128-byte line per
 // column of the output (256 rows x 4 bits), so its codes and scales are
 // collected in LDS and written at the end with 16-byte stores, 8 whole lines per
@@ -419,8 +420,9 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
   constexpr int SPC = MX ? kStripRows / 32 : kStripRows / 16;
   // 16-byte accesses (staging, line collection, write-out) need 16-byte alignment
   __shared__ f32x2 tab[128];
-  __shared__ __attribute__((aligned(16))) uint32_t lds_v[64 * VP];
-  __shared__ __attribute__((aligned(16))) uint32_t lds_w[SR ? 64 * WP : 1];
+  // (16x16 tiles need no staging: their column copy is the row copy transposed)
+  __shared__ __attribute__((aligned(16))) uint32_t lds_v[TWO_D ? 1 : 64 * VP];
+  __shared__ __attribute__((aligned(16))) uint32_t lds_w[SR && !TWO_D ? 64 * WP : 1];
   __shared__ __attribute__((aligned(16))) uint32_t col_codes[64 * CP];
   __shared__ __attribute__((aligned(16))) uint32_t col_scales[TWO_D ? TR : 64 * SPC / 4];
   __shared__ float lds_m[MX ? 4 * 64 : 1];  // MXFP4: column maxima of each wave's 16 rows
@@ -529,6 +531,17 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
     }
     if (!p.emit_col) return;  // uniform across the workgroup
 
+    // ---- 16x16 tiles: the column copy shares the tile's scale, reciprocal,
+    // 4/6 choice and every element's word, so its codes are the row copy's,
+    // transposed inside the tile (in registers, across the lanes of the DPP row)
+    if constexpr (TWO_D) {
+      const BlockCodes cc = transpose_tile16(res.codes, i);
+      const int col = 16 * bj + i;
+      *reinterpret_cast<uint2*>(col_codes + col * CP + 8 * q + 2 * bi) = make_uint2(cc.lo, cc.hi);
+      if (i == 0) reinterpret_cast<uint8_t*>(col_scales)[bj * TR + 4 * q + bi] = (uint8_t)res.sb;
+      return;
+    }
+
     // ---- stage the sub-tile (and its random words) in LDS
     {
       const int row = 16 * bi + i;
@@ -585,18 +598,6 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
     if constexpr (MX) {
       sbc = mx_scale_code(fmaxf(mcol, lds_m[(bi ^ 1) * 64 + col]));
       cc = mx_round16<SR>(y, sbc, w);
-    } else if constexpr (TWO_D) {
-      // same values, same reciprocal, same words: the codes of the row copy, transposed
-      if constexpr (SR && RULE != kRuleNone) {
-        cc = round16_sr_chosen(y, res.e, w, res.four);
-      } else {
-        if constexpr (SR) {
-#pragma unroll
-          for (int k = 1; k < 16; k += 2) w[k] >>= 1;
-        }
-        cc = round16<SR>(y, res.e, w);
-      }
-      sbc = res.sb;
     } else {
       const BlockResult rc = quant_block16<SR, RULE, true>(y, w, tab, ts.den6, ts.den4);
       cc = rc.codes;
@@ -607,8 +608,6 @@ __global__ __launch_bounds__(kThreads) void quant_strip_kernel(const void* __res
     uint8_t* csb = reinterpret_cast<uint8_t*>(col_scales);
     if constexpr (MX) {
       if ((bi & 1) == 0) csb[col * SPC + 2 * q + (bi >> 1)] = (uint8_t)sbc;
-    } else if constexpr (TWO_D) {
-      if (i == 0) csb[bj * TR + 4 * q + bi] = (uint8_t)sbc;
     } else {
       csb[col * SPC + 4 * q + bi] = (uint8_t)sbc;
     }

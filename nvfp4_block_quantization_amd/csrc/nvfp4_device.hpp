@@ -273,6 +273,56 @@ struct BlockCodes {
   uint32_t lo, hi;  // 16 packed codes: element 2k in bits 4k..4k+3 of the 64-bit pair
 };
 
+// Transpose of a 16x16 tile of codes held by the 16 lanes of a DPP row: lane i
+// (i = lane & 15) brings row i (code c in nibble c) and gets column i (the code
+// of row r in nibble r).  Each of four exchange stages swaps one bit of the row
+// index with the same bit of the column index: a code whose two bits differ
+// moves to lane i ^ b and nibble c ^ b (b = 8: whole words, with lane i ^ 8;
+// b = 4, 2: byte selects with lanes i ^ 4 and i ^ 2; b = 1: nibbles, lane i ^ 1).
+__device__ __forceinline__ uint32_t lane_xor8(uint32_t v) {  // row_ror:8 inside a 16-lane row
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t lane_xor4(uint32_t v) {  // ds_swizzle bitmask mode: and 0x1F, xor 4
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x101F);
+}
+__device__ __forceinline__ uint32_t lane_xor2(uint32_t v) {  // quad_perm [2,3,0,1]
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t lane_xor1(uint32_t v) {  // quad_perm [1,0,3,2]
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ BlockCodes transpose_tile16(BlockCodes x, int i) {
+  uint32_t lo = x.lo, hi = x.hi;
+  {  // b = 8: lanes below 8 keep their low word and take the partner's as high word
+    const bool up = (i & 8) != 0;
+    const uint32_t recv = lane_xor8(up ? lo : hi);
+    lo = up ? recv : lo;
+    hi = up ? hi : recv;
+  }
+  {  // b = 4: 16-bit halves; v_perm bytes 0-3 from the own word, 4-7 from the partner's
+    const uint32_t sel = (i & 4) ? 0x03020706u : 0x05040100u;
+    const uint32_t plo = lane_xor4(lo), phi = lane_xor4(hi);
+    lo = __builtin_amdgcn_perm(plo, lo, sel);
+    hi = __builtin_amdgcn_perm(phi, hi, sel);
+  }
+  {  // b = 2: bytes
+    const uint32_t sel = (i & 2) ? 0x03070105u : 0x06020400u;
+    const uint32_t plo = lane_xor2(lo), phi = lane_xor2(hi);
+    lo = __builtin_amdgcn_perm(plo, lo, sel);
+    hi = __builtin_amdgcn_perm(phi, hi, sel);
+  }
+  {  // b = 1: nibbles; the partner's word rotated by 4 bits toward the taken nibbles
+    const bool odd = (i & 1) != 0;
+    const uint32_t keep = odd ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
+    const uint32_t sh = odd ? 4u : 28u;
+    const uint32_t plo = lane_xor1(lo), phi = lane_xor1(hi);
+    lo = (lo & keep) | (__builtin_amdgcn_alignbit(plo, plo, sh) & ~keep);
+    hi = (hi & keep) | (__builtin_amdgcn_alignbit(phi, phi, sh) & ~keep);
+  }
+  return BlockCodes{lo, hi};
+}
+
 // Pairwise sum of 16 values in index order.
 __device__ __forceinline__ float pairwise16(const float* t) {
   float s[8];
@@ -380,19 +430,6 @@ __device__ __forceinline__ CodePair round16_sr_both(const float* y, float e6, fl
   cp.c4.lo = nibble_merge(P[0] >> 4, P[1]);
   cp.c4.hi = nibble_merge(P[2] >> 4, P[3]);
   return cp;
-}
-
-// The codes of the candidate already chosen (four = 1: scale to 4), rounded
-// with that candidate's bits of each word: both slots get the same scaled value
-// and the chosen slot's nibbles are kept.
-__device__ __forceinline__ BlockCodes round16_sr_chosen(const float* y, float e, const uint32_t* w, uint32_t four) {
-  uint32_t P[4];
-  sr_pair_regs(y, e, e, w, P);
-  const uint32_t s0 = four << 2, s1 = 4u - s0;
-  BlockCodes c;
-  c.lo = nibble_merge(P[0] >> s0, P[1] << s1);
-  c.hi = nibble_merge(P[2] >> s0, P[3] << s1);
-  return c;
 }
 
 // Per-element error terms of one candidate: t_i = eps_i^2 (MSE) or |eps_i|
