@@ -303,8 +303,8 @@ struct RowChunk {
         __builtin_amdgcn_raw_buffer_store_b8((uint8_t)code, rsc, (lb & 1) == 0 ? (lb >> 1) : kDrop, 0, 0);
       } else {
         // 4/6 decided from the error estimates where they suffice, as in the
-        // strip kernel (5 more VGPRs, a wave less per SIMD; still 2-3% faster on
-        // the 1x16 activation shape, even on the gradient shape)
+        // strip kernel: 5 more VGPRs (a wave less per SIMD), yet 2-3% faster on
+        // the 1x16 activation shape and as fast on the gradient shape
         const BlockResult r = quant_block16<SR, RULE, true>(y, w, tab, ts.den6, ts.den4);
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{r.codes.lo, r.codes.hi}, rc, 8u * lb, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b8((uint8_t)r.sb, rsc, lb, 0, 0);
@@ -348,13 +348,14 @@ __global__ __launch_bounds__(kThreads) void quant_row_kernel(const void* __restr
 // 16x16 block g: one block row per lane in the row pass, one block column per
 // lane in the column pass; every LDS exchange of a sub-tile stays inside one
 // wave (wave w owns rows 16w .. 16w + 15 in both passes), so waves run free of
-// each other until the strip's end.  16x16 tiles need no column pass: the
-// column copy's codes are the row copy's, transposed across the DPP row.  The row copy is stored straight from
-// registers.  The column copy of a 256-row strip is one full 128-byte line per
-// column of the output (256 rows x 4 bits), so its codes and scales are
-// collected in LDS and written at the end with 16-byte stores, 8 whole lines per
-// wave instruction.  The input is read once, with streaming (non-temporal)
-// loads that do not displace the partly written output lines from the L2.
+// each other until the strip's end (16x16 tiles need no column pass: their
+// column copy's codes are the row copy's, transposed across the DPP row).  The
+// row copy is stored straight from registers.  The column copy of a 256-row
+// strip is one full 128-byte line per column of the output (256 rows x 4
+// bits), so its codes and scales are collected in LDS and written at the end
+// with 16-byte stores, 8 whole lines per wave instruction.  The input is read
+// once, with streaming (non-temporal) loads that do not displace the partly
+// written output lines from the L2.
 constexpr int kStripRows = 256;
 
 // Wave-private LDS exchange: wait until this wave's LDS accesses have completed
