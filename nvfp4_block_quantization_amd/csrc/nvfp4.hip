@@ -1141,7 +1141,8 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dtype_arg, int64_t rows, 
             // dispatcher balance the chunks over the CUs (a persistent grid gives
             // some workgroups one chunk more than others).  Lighter chunks keep
             // the persistent grid, whose prefetch hides the load latency.
-            int64_t grid = SR() ? nchunks : resident_grid(k);
+            // (the grid size is a 32-bit count: beyond 2^30 chunks, persistent)
+            int64_t grid = SR() && nchunks <= (1ll << 30) ? nchunks : resident_grid(k);
             if (grid > nchunks) grid = nchunks;
             hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), 0, s, x, nblocks, p);
           });
