@@ -380,18 +380,38 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_kernel(const uint8_t* __rest
       nv_scales(wsa[i], sca[i]);
       nv_scales(wsb[i], scb[i]);
     }
+    // chunk c + 1's operands are expanded while chunk c's 16 products run: two
+    // operand sets alternate, and each product is followed by four of the
+    // expansion's 64 instructions
+    v8h fa[2][4], fb[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fa[0][i] = nv_half8(word_of(qa[i], 0), sca[i][0]);
+      fb[0][i] = nv_half8(word_of(qb[i], 0), scb[i][0]);
+    }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {  // 16-value chunk c: word c of the lane's 8, block c / 2
-      v8h fa[4], fb[4];
+      const int cur = c & 1;
+      if (c < 7) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        fa[i] = nv_half8(word_of(qa[i], c), sca[i][c >> 1]);
-        fb[i] = nv_half8(word_of(qb[i], c), scb[i][c >> 1]);
+        for (int i = 0; i < 4; ++i) {
+          fa[cur ^ 1][i] = nv_half8(word_of(qa[i], c + 1), sca[i][(c + 1) >> 1]);
+          fb[cur ^ 1][i] = nv_half8(word_of(qb[i], c + 1), scb[i][(c + 1) >> 1]);
+        }
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+      if (c < 7) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     NV_WAIT_VM_LGKM0(24);  // this thread's loads of step s + 1 have landed; steps s + 2, s + 3 pending
     __builtin_amdgcn_s_barrier();
