@@ -2,8 +2,8 @@
  * nvfp4_membench.h -- HBM stream kernels of libnvfp4_membench.so, the
  * measurement companion of libnvfp4.so (not part of the quantization ABI).
  *
- * They give the bandwidth ceilings a memory-bound kernel on this GPU is judged
- * against: a read-only stream, a write-only stream and a copy, each moving 16
+ * They measure the bandwidth ceilings a memory-bound kernel on this GPU is
+ * compared with: a read-only stream, a write-only stream and a copy, each moving 16
  * bytes per lane per access from a persistent grid of workgroups that walk the
  * buffer in grid-stride order with several accesses in flight per lane.  Also
  * used as the known-size kernels that scale the profiler's HBM byte counters.
