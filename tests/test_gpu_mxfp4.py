@@ -173,3 +173,31 @@ def test_mxfp4_full_size_whole():
     assert int(out["scales_row"].max().item()) <= 252 and int(out["scales_col"].max().item()) <= 252
     del xg, out, out2
     torch.cuda.empty_cache()
+
+
+def test_mxfp4_full_size_row_copy_rne():
+    """8192x4096 bf16 (the activation with outlier columns), the MXFP4 row copy
+    alone with round-to-nearest, which the row kernel computes: every output
+    byte against the oracle, then a rerun that must write the same bytes."""
+    c = workloads.CONFIGS[2]
+    rows, cols = c["rows"], c["cols"]
+    say(f"mx row copy full size: generating {rows}x{cols}")
+    x = workloads.inputs(c, seed=0)
+    xg = to_gpu(x)
+    say("mx row copy full size: GPU quantize")
+    out = nv.mxfp4_quantize(xg, rowwise=True, colwise=False, sr=False)
+    torch.cuda.synchronize()
+    say("mx row copy full size: oracle in row bands")
+    ref = _oracle_mx_bands(x, rows, cols, sr=False)
+    for k in ("codes_row", "scales_row"):
+        got = out[k].cpu().numpy()
+        if not np.array_equal(got, ref[k]):
+            bad = np.argwhere(got != ref[k])
+            raise AssertionError(f"mx row copy full size: {k} differs at {len(bad)} places, first {bad[:5].tolist()}")
+    say("mx row copy full size: determinism rerun")
+    out2 = nv.mxfp4_quantize(xg, rowwise=True, colwise=False, sr=False)
+    torch.cuda.synchronize()
+    for k in ("codes_row", "scales_row"):
+        assert torch.equal(out[k], out2[k]), k
+    del xg, out, out2
+    torch.cuda.empty_cache()
