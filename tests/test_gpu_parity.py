@@ -262,3 +262,29 @@ def test_full_size_workloads_whole(k):
         assert np.array_equal(f32_bits(d.cpu().numpy()), f32_bits(r))
     del xg, out, out2, ref
     torch.cuda.empty_cache()
+
+
+def test_full_size_dequantize_workload5_row_copy():
+    """The row copy of the 65536x8192 activation, dequantized on the GPU (the
+    launch the benchmark times), against the oracle's dequantization of the
+    same codes, scales and tensor scale: every value bit for bit."""
+    c = with_mask(FULL[5])
+    rows, cols = c["rows"], c["cols"]
+    tag = "full dequantize workload 5"
+    say(f"{tag}: generating {rows}x{cols}")
+    x = workloads.inputs(c, seed=0)
+    xg = to_gpu(x)
+    del x
+    say(f"{tag}: GPU amax + quantize + dequantize")
+    _, out = gpu_quantize(xg, c)
+    del xg
+    d = nv.dequantize(out["codes_row"], out["scales_row"], out["tensor_scale"], rows, cols)
+    torch.cuda.synchronize()
+    got = d.cpu().numpy()
+    codes, scales = out["codes_row"].cpu().numpy(), out["scales_row"].cpu().numpy()
+    s_t = float(out["tensor_scale"].cpu().numpy()[0])
+    del d, out
+    torch.cuda.empty_cache()
+    say(f"{tag}: oracle dequantize")
+    ref = oracle.dequantize(codes, scales, s_t, rows, cols)
+    _assert_same(tag, "dequantized", f32_bits(got), f32_bits(ref))
